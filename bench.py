@@ -1,0 +1,149 @@
+"""Benchmark: fused exact attention forward on one MI355X.
+
+One step = one attn_fwd call over the whole workload (every head, every
+query block, the full key loop), inputs resident in device memory.  The
+default workload is the long-sequence causal case B=1, H=16, N=16384,
+d=128, bf16.  Throughput counts 4*B*H*N^2*d FLOPs, halved for causal.
+
+Prints one JSON line.  ``roofline`` compares the measured rate with the
+published dense bf16 matrix-core peak; ``traffic`` is taken from a committed
+counter summary only while the kernel sources it was measured on are
+unchanged (else null).  ``cpu_baseline`` times the float64 CPU oracle on a
+bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # published MI355X dense peaks
+HBM_GBPS = 8000.0
+KERNEL_SOURCES = ["exact_attention_127_amd/csrc/attn_mfma_bf16.hip",
+                  "exact_attention_127_amd/csrc/common.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """Per-launch HBM bytes from a committed counter summary, if still valid."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
+    """The float64 oracle on whole heads of the workload until ~budget_s elapse."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = inp["workload"]
+    rows = np.arange(w.N)
+    flops_head = w.flops / (w.B * w.H)
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            oracle.attention_rows(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
+                                  inp["scale"], w.causal, rows)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * flops_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} heads (all {w.N} query rows each), float64 numpy, "
+                      f"{dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_causal_16k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(heads are independent, so several GPUs would each run this kernel on "
+              "their share of heads)", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_127_amd as A
+    from seeded_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench.py times the bf16 workloads", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    q, k, v = (torch.from_numpy(inp[x]).to(dev).to(torch.bfloat16).contiguous() for x in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        A.attn_fwd(q, k, v, o=o, lse=lse, scale=w.scale, causal=w.causal, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps          # one launch per step
+    ms_per_step = wall * 1e3 / args.steps
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    line = {
+        "metric": "attn fwd TFLOP/s + % of bf16 MFMA peak, B=1 H=16 N=16384 d=128 causal"
+        if args.workload == "long_causal_16k" else f"attn fwd TFLOP/s, {args.workload}",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "seed": w.seed, "flops_per_step": w.flops,
+                   "pct_of_bf16_peak": round(100 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_from_profile(w.name),
+                     "kernel_ms": round(kernel_ms, 4), "kernel_hash": kernel_hash()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,172 @@
+"""Python binding of the fused exact-attention library (``libattn127.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn.h``.  torch supplies the
+device memory and the current stream; there is no CPU or framework fallback,
+and a missing library raises ``AttnLibraryMissing``.
+
+The functions keep the C names:
+
+    attn_fwd(q, k, v, o=None, lse=None, scale=None, causal=False)
+    attn_fwd_simple(...)                       same contract, plain kernel
+    attn_fp8_prepare(q, k, v, R)               -> (q8, k8, v8, sq, sk, sv)
+    attn_fwd_fp8(q8, k8, v8, sq, sk, sv, ...)  -> (o, lse)
+    attn_strerror(status)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime that the library then shares
+
+__all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
+           "attn_strerror", "AttnError", "AttnLibraryMissing", "lib", "LIB_PATH",
+           "EXPORTED_SYMBOLS", "ATTN_F32", "ATTN_BF16", "FP8_TILE"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn127.so")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
+                    "attn_strerror")
+ATTN_F32, ATTN_BF16 = 0, 1
+FP8_TILE = 128
+_STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
+           -3: "ATTN_ERR_HIP"}
+
+
+class AttnLibraryMissing(RuntimeError):
+    pass
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({attn_strerror(status)})")
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise AttnLibraryMissing(
+                f"{LIB_PATH} is missing: build it with `python -m exact_attention_127_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        fwd_args = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]
+        for name in ("attn_fwd", "attn_fwd_simple"):
+            fn = getattr(L, name)
+            fn.argtypes = fwd_args
+            fn.restype = _I
+        L.attn_fp8_prepare.argtypes = [_P] * 10 + [_I, _I, _I, _I, _P]
+        L.attn_fp8_prepare.restype = _I
+        L.attn_fwd_fp8.argtypes = [_P] * 8 + [_I, _I, _I, _I, _F, _I, _P]
+        L.attn_fwd_fp8.restype = _I
+        L.attn_strerror.argtypes = [_I]
+        L.attn_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def attn_strerror(status: int) -> str:
+    return lib().attn_strerror(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise AttnError(status, where)
+
+
+def _fwd(name, q, k, v, o, lse, scale, causal, stream, with_lse):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for t in (q, k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    if q.dtype == torch.bfloat16:
+        dtype = ATTN_BF16
+    elif q.dtype == torch.float32:
+        dtype = ATTN_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                              float(scale), int(bool(causal)), dtype, _stream(stream))
+    _check(st, name)
+    return o, lse
+
+
+def attn_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None, with_lse=True):
+    """O (and LSE) of softmax(Q K^T * scale) V on matrix cores (bf16) or in float32."""
+    return _fwd("attn_fwd", q, k, v, o, lse, scale, causal, stream, with_lse)
+
+
+def attn_fwd_simple(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None,
+                    with_lse=True):
+    """The same operation on the plain float32-arithmetic kernel."""
+    return _fwd("attn_fwd_simple", q, k, v, o, lse, scale, causal, stream, with_lse)
+
+
+def attn_fp8_prepare(q, k, v, R, stream=None):
+    """Rotate Q, K by R and quantise Q, K, V to e4m3 with one scale per 128-token tile."""
+    B, H, N, d = q.shape
+    for t in (q, k, v):
+        if t.shape != q.shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous float32 [B, H, N, d]")
+    if R.shape != (d, d) or R.dtype != torch.float32 or not R.is_contiguous():
+        raise ValueError("R must be contiguous float32 [d, d]")
+    nt = -(-N // FP8_TILE)
+    codes = [torch.empty((B, H, N, d), dtype=torch.uint8, device=q.device) for _ in range(3)]
+    scales = [torch.empty((B, H, nt), dtype=torch.float32, device=q.device) for _ in range(3)]
+    st = lib().attn_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(R), *map(_ptr, codes),
+                                *map(_ptr, scales), B, H, N, d, _stream(stream))
+    _check(st, "attn_fp8_prepare")
+    return (*codes, *scales)
+
+
+def attn_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, scale=None, causal=False,
+                 stream=None, with_lse=True):
+    """Attention on e4m3 codes with per-tile scales; O is bf16."""
+    B, H, N, d = q8.shape
+    for t in (q8, k8, v8):
+        if t.shape != q8.shape or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 [B, H, N, d]")
+    nt = -(-N // FP8_TILE)
+    for s in (sq, sk, sv):
+        if s.shape != (B, H, nt) or s.dtype != torch.float32 or not s.is_contiguous():
+            raise ValueError("scales must be contiguous float32 [B, H, ceil(N/128)]")
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv),
+                            _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+                            _stream(stream))
+    _check(st, "attn_fwd_fp8")
+    return o, lse

@@ -1,0 +1,113 @@
+// C ABI of the attention library: argument checks and kernel dispatch.
+// Every check runs on the host before any HIP call, so a rejected call has
+// no device side effect; the library holds no state and allocates nothing.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point; returns ATTN_OK, an error, or 1
+// for "nothing to do".
+int check_shape(int B, int H, int N, int d) {
+  if (B < 0 || H < 0 || N < 0) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_INVALID_ARG;
+  if (N >= (1 << 30)) return ATTN_ERR_INVALID_ARG;
+  const int64_t bh = static_cast<int64_t>(B) * H;
+  if (bh >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  // grid: one workgroup per (b, h, 64-row block) at most
+  if (bh * ((static_cast<int64_t>(N) + 63) / 64) >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  if (B == 0 || H == 0 || N == 0) return 1;
+  return ATTN_OK;
+}
+
+int check_scale(float scale) {
+  return (std::isfinite(scale) && scale > 0.f) ? ATTN_OK : ATTN_ERR_INVALID_ARG;
+}
+
+int check_ptrs(const void* q, const void* k, const void* v, const void* o, const void* lse) {
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+int fwd_common(bool simple, const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (check_scale(scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (check_ptrs(q, k, v, o, lse) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (st == 1) return ATTN_OK;
+  attn127::LaunchArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, dtype, stream};
+  if (simple || dtype == ATTN_F32) return status_of(attn127::launch_simple(a));
+  return status_of(attn127::launch_mfma_bf16(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int N, int d, float scale, int causal, int dtype, void* stream) {
+  return fwd_common(false, q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream);
+}
+
+int attn_fwd_simple(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  return fwd_common(true, q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream);
+}
+
+int attn_fp8_prepare(const float* q, const float* k, const float* v, const float* R, uint8_t* q8,
+                     uint8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, float* v_scale,
+                     int B, int H, int N, int d, void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (!q || !k || !v || !R || !q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale)
+    return ATTN_ERR_INVALID_ARG;
+  const void* ps[] = {q, k, v, R, q8, k8, v8};
+  for (const void* p : ps)
+    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  const void* ss[] = {q_scale, k_scale, v_scale};
+  for (const void* p : ss)
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return ATTN_ERR_INVALID_ARG;
+  if (st == 1) return ATTN_OK;
+  attn127::Fp8PrepArgs a{q, k, v, R, q8, k8, v8, q_scale, k_scale, v_scale, B, H, N, d, stream};
+  return status_of(attn127::launch_fp8_prepare(a));
+}
+
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                 const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (check_scale(scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (check_ptrs(q8, k8, v8, o, lse) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
+  const void* ss[] = {q_scale, k_scale, v_scale};
+  for (const void* p : ss)
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return ATTN_ERR_INVALID_ARG;
+  if (st == 1) return ATTN_OK;
+  attn127::Fp8Args a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale,
+                     causal ? 1 : 0, stream};
+  return status_of(attn127::launch_fp8_fwd(a));
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size, dtype or scale)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

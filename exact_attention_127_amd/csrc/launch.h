@@ -1,0 +1,56 @@
+// Host-side launch descriptors shared by the C ABI and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn127 {
+
+struct LaunchArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // nullable
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;           // attn_dtype
+  void* stream;
+};
+
+struct Fp8Args {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* sq;
+  const float* sk;
+  const float* sv;
+  void* o;             // bf16
+  float* lse;          // nullable
+  int B, H, N, d;
+  float scale;
+  int causal;
+  void* stream;
+};
+
+struct Fp8PrepArgs {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* R;
+  uint8_t* q8;
+  uint8_t* k8;
+  uint8_t* v8;
+  float* sq;
+  float* sk;
+  float* sv;
+  int B, H, N, d;
+  void* stream;
+};
+
+hipError_t launch_simple(const LaunchArgs& a);
+hipError_t launch_mfma_bf16(const LaunchArgs& a);
+hipError_t launch_fp8_prepare(const Fp8PrepArgs& a);
+hipError_t launch_fp8_fwd(const Fp8Args& a);
+
+}  // namespace attn127

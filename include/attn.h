@@ -1,0 +1,132 @@
+/*
+ * attn.h -- C ABI of the fused exact-attention forward library (gfx950).
+ *
+ * The operation (page "Self-Attention, CUDA kernels and FlashAttention",
+ * section 1): for every batch b and head h, with Q, K, V the N x d slices
+ * [b][h],
+ *
+ *     S = Q K^T * scale,   P = row-softmax(S),   O = P V
+ *
+ * and (same page, section 3) only O and one small statistic per query row
+ * are written: the natural-log log-sum-exp of that row's scaled, masked
+ * scores, LSE_i = ln sum_j exp(S_ij).  The N x N matrices S and P never go to
+ * device memory.  Heads are independent and run in parallel (section 1,
+ * multi-head paragraph); query blocks of one head run in parallel too
+ * (page "FlashAttention scaling, multi-GPU training and weight
+ * quantization", section 1, the sequence-length-parallelism bullet).
+ *
+ * Common conventions
+ *   Layout     q, k, v, o: contiguous row-major [B][H][N][d]; lse: [B][H][N].
+ *              Element (b,h,i,c) sits at ((b*H + h)*N + i)*d + c.
+ *   Causal     causal != 0 masks key j for query i when j > i (square
+ *              self-attention: row i sees keys 0..i).
+ *   Scale      scale must be finite and > 0 (the pages use 1/sqrt(d)).
+ *   Sizes      B, H, N >= 0 (any zero makes the call a no-op that returns
+ *              ATTN_OK); d must be 64 or 128; B*H*N*d < 2^31 is not needed
+ *              (offsets are 64-bit), but B*H < 2^31 and N < 2^30.
+ *   Pointers   device pointers, 16-byte aligned, owned by the caller; the
+ *              library allocates, frees and retains nothing and keeps no
+ *              global state, so calls on different streams are independent.
+ *              lse may be NULL (the statistic is then not written).  Inputs
+ *              must not alias outputs.
+ *   Stream     a hipStream_t passed as void* (NULL = the null stream).  Every
+ *              call only enqueues work and returns; the caller synchronises.
+ *   Errors     a negative attn_status.  Arguments are checked on the host
+ *              before any HIP call, so a rejected call has no device side
+ *              effect.  ATTN_ERR_HIP reports a failed launch; faults during
+ *              execution surface at the caller's synchronisation.
+ */
+#ifndef ATTN127_ATTN_H
+#define ATTN127_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F32 = 0,   /* q, k, v, o are float32                                  */
+  ATTN_BF16 = 1   /* q, k, v, o are bfloat16 (bit pattern in uint16)        */
+} attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,  /* null / misaligned pointer, bad size or scale */
+  ATTN_ERR_UNSUPPORTED = -2,  /* valid request this build has no kernel for  */
+  ATTN_ERR_HIP = -3           /* the HIP runtime rejected a launch            */
+} attn_status;
+
+/*
+ * attn_fwd -- O = softmax(Q K^T * scale) V and LSE for all B*H heads.
+ *
+ * dtype ATTN_BF16 runs the matrix-core kernel: both products on bf16 MFMA
+ * with float32 accumulation, the online softmax (running row maximum and
+ * running normaliser, the partial output rescaled as each key tile arrives;
+ * page "Self-Attention, CUDA kernels and FlashAttention", section 3) in
+ * float32, P rounded to bf16 (nearest-even) as the second product's operand,
+ * the 1/normaliser division done once after the last key tile (page
+ * "FlashAttention scaling, multi-GPU training and weight quantization",
+ * section 1, the bullet on fewer non-matmul operations), O rounded to bf16
+ * (nearest-even).  dtype ATTN_F32 keeps every step in float32 (no bf16
+ * rounding anywhere).  lse is float32 in both cases.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, float scale, int causal, int dtype,
+             void* stream);
+
+/*
+ * attn_fwd_simple -- the same operation and contract as attn_fwd, computed
+ * by a plain tiled kernel with float32 vector arithmetic (no matrix cores,
+ * no bf16 rounding of P).  A second, structurally different device path,
+ * kept for cross-checking; not tuned.
+ */
+int attn_fwd_simple(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int H, int N, int d, float scale,
+                    int causal, int dtype, void* stream);
+
+/* Tokens per fp8 quantisation tile: one float32 scale per (b, h, tile). */
+#define ATTN_FP8_TILE 128
+
+/*
+ * attn_fp8_prepare -- block quantisation with incoherent processing (page
+ * "FlashAttention scaling, multi-GPU training and weight quantization",
+ * section 1, the FP8 bullet).
+ *
+ *   q', k' = q R, k R      R: float32 [d][d] row-major, orthogonal (caller's
+ *                          seeded draw; the product is not checked); v is
+ *                          not rotated.
+ *   For each (b, h, t) with tile t = tokens [128 t, 128 t + 128) of all d
+ *   channels:  s = amax / 448 (s = 1 when amax = 0), code = e4m3(x / s)
+ *   (OCP E4M3FN, nearest-even, saturating to +-448).
+ *
+ * q, k, v: float32 [B][H][N][d].  q8, k8, v8: uint8 codes [B][H][N][d].
+ * q_scale, k_scale, v_scale: float32 [B][H][ceil(N/128)].
+ */
+int attn_fp8_prepare(const float* q, const float* k, const float* v,
+                     const float* R, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                     float* q_scale, float* k_scale, float* v_scale,
+                     int B, int H, int N, int d, void* stream);
+
+/*
+ * attn_fwd_fp8 -- attention on the e4m3 tensors attn_fp8_prepare writes.
+ * Value of an input element = decode(code) * scale of its 128-token tile.
+ * Both products run on fp8 MFMA with float32 accumulation; P is quantised
+ * to e4m3 as the second product's operand; the tile scales of Q, K and V are
+ * applied in float32 inside the softmax and the rescale.  o is bf16
+ * [B][H][N][d]; lse (nullable) float32 [B][H][N].  Other conventions as
+ * attn_fwd.
+ */
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                 const float* q_scale, const float* k_scale,
+                 const float* v_scale, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN127_ATTN_H */

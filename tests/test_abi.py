@@ -1,0 +1,80 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/attn.h declares, and rejects bad arguments before any HIP call
+(so these calls are safe on a host without a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_127_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(A.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = A.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_strerror():
+    assert A.attn_strerror(0) == "ok"
+    for s in (-1, -2, -3):
+        assert len(A.attn_strerror(s)) > 5
+    assert A.attn_strerror(12345) == "unknown status"
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: checks fail first
+
+
+def _fwd(fn, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=1, N=8, d=64, scale=0.125,
+         causal=0, dtype=1):
+    return getattr(A.lib(), fn)(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_simple"])
+@pytest.mark.parametrize("bad", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None),
+    dict(q=FAKE + 2), dict(o=FAKE + 8), dict(lse=FAKE + 2),
+    dict(d=32), dict(d=96), dict(d=0), dict(N=-1), dict(B=-1), dict(H=-2),
+    dict(dtype=2), dict(dtype=-1), dict(scale=0.0), dict(scale=-1.0),
+    dict(scale=float("inf")), dict(scale=float("nan")), dict(N=1 << 30),
+])
+def test_invalid_arguments_rejected(fn, bad):
+    assert _fwd(fn, **bad) == -1
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_simple"])
+@pytest.mark.parametrize("empty", [dict(B=0), dict(H=0), dict(N=0)])
+def test_empty_is_a_noop(fn, empty):
+    # zero work: returns before any HIP call, so no device is needed
+    assert _fwd(fn, **empty) == 0
+
+
+def test_fp8_entry_points_validate():
+    L = A.lib()
+    args = [FAKE] * 10
+    assert L.attn_fp8_prepare(*args, 1, 1, 8, 48, None) == -1
+    assert L.attn_fp8_prepare(*([None] + args[1:]), 1, 1, 8, 64, None) == -1
+    assert L.attn_fp8_prepare(*args, 0, 1, 8, 64, None) == 0
+    f = [FAKE] * 7 + [None]
+    assert L.attn_fwd_fp8(*f, 1, 1, 8, 128, -0.5, 0, None) == -1
+    assert L.attn_fwd_fp8(*f, 1, 1, 8, 100, 0.1, 0, None) == -1
+    assert L.attn_fwd_fp8(*f, 1, 0, 8, 128, 0.1, 0, None) == 0
+
+
+def test_grid_limit_rejected():
+    # B*H*ceil(N/64) would not fit a 1-D grid
+    assert _fwd("attn_fwd", B=1 << 15, H=1 << 15, N=64 * 4) == -1
