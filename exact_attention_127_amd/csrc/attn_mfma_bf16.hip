@@ -8,26 +8,33 @@
 // and an inner loop over key/value tiles of BC keys.  Per tile:
 //   S^T = K Q^T        bf16 MFMA 32x32x16, float32 accumulate
 //   online softmax     running row maximum m and normaliser l in registers,
-//                      p = exp2(S*c - m) with c = scale*log2(e), the partial
-//                      output rescaled by exp2(m_old - m_new)
+//                      p = exp2(S*c - m) with c = scale*log2(e)
 //   O^T += V^T P^T     P rounded to bf16, bf16 MFMA, float32 accumulate
 // and after the last tile O /= l once, O rounded to bf16, LSE = ln2*(m+log2 l).
 // S and P live only in registers; nothing N x N reaches memory.
 //
-// Layout choices (gfx950, wave64):
-//  * Scores are computed transposed (keys x queries), so in the 32x32
-//    accumulator layout each lane holds 16 keys of ONE query (column
-//    lane%32); the row maximum and row sum are in-lane reductions plus one
+// gfx950 mapping:
+//  * Scores are computed transposed (keys x queries): in the 32x32
+//    accumulator layout each lane then holds 16 keys of ONE query (column
+//    lane%32), so the row maximum and row sum are in-lane reductions plus one
 //    v_permlane32_swap between the two lane halves.
-//  * Those probabilities feed the second product directly as the B operand
-//    (keys x queries); the key order inside each 16-key MFMA step is the
-//    accumulator's order, so V^T is written to LDS in that same permuted key
-//    order and every A-operand read is one 16-byte ds_read.
-//  * Q is loaded once into registers (B operand of the first product); K is
-//    staged row-major in LDS, V transposed; both double-buffered so tile t+1
-//    is fetched from HBM while tile t is computed, with one barrier per tile.
-//  * Rows are padded by 16 bytes so the 16-byte A-operand reads of 16 lanes
-//    cover all LDS banks once.
+//  * Those probabilities feed the second product directly as its B operand;
+//    its A operand (V^T) comes from row-major V in LDS through
+//    ds_read_b64_tr_b16, which hands each lane four keys of one channel, read
+//    in exactly the key order the accumulator registers hold.
+//  * K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16
+//    bytes per lane, no register staging), double-buffered so tile t+1 is in
+//    flight while tile t is computed; one barrier per tile.  Out-of-range
+//    rows of the last tile read as zero (buffer bounds).  16-byte chunks are
+//    XOR-swizzled per row so the matrix-operand reads hit distinct banks.
+//  * The running maximum used as the exponent reference is only raised when
+//    some row's tile maximum exceeds it by more than 2^kTau (base 2); p then
+//    stays <= 2^kTau, the normaliser and the partial output carry the same
+//    reference, and the single division at the end cancels it exactly.  Most
+//    tiles of a long row therefore skip the rescale of the partial output.
+//  * Work items are grouped by XCD (dispatch is round-robin over the 8 XCDs)
+//    so the query blocks of one head share one L2, heaviest causal blocks
+//    first.
 #include "common.h"
 #include "launch.h"
 
@@ -39,86 +46,73 @@ constexpr int BRW = 32;          // query rows per wave
 constexpr int BR = NW * BRW;     // query rows per workgroup
 constexpr int BC = 64;           // keys per tile
 constexpr int NT = NW * 64;      // threads per workgroup
+constexpr float kTau = 8.0f;     // allowed growth of p above 1, as a power of two
+constexpr int kXcds = 8;
 
 template <int D>
-struct Smem {
-  static constexpr int KROW = D * 2 + 16;           // bytes per K row in LDS
-  static constexpr int VROW = BC * 2 + 16;          // bytes per V^T row in LDS
-  static constexpr int KBYTES = BC * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int TOTAL = 2 * STAGE;
-  static constexpr int KCHUNKS = BC * D / 8 / NT;   // 16-byte K chunks per thread
-  static constexpr int VTHREADS = (BC / 4) * (D / 8);  // threads owning a 4x8 V block
+struct Cfg {
+  static constexpr int ROWB = D * 2;           // bytes per K/V row
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPB = 1024 / ROWB;      // rows per 1 KB load block
+  static constexpr int TILEB = BC * ROWB;      // bytes of one K (or V) tile
+  static constexpr int BLK = TILEB / 1024;     // 1 KB blocks per tile
+  static constexpr int BPW = BLK / NW;         // blocks per wave per tile
+  static_assert(BPW * NW == BLK, "tile must split evenly over the waves");
 };
 
-// Position of key kk (0..BC-1) inside the V^T row: within each 16-key group
-// the 4-key groups 1 and 2 trade places, matching which keys a lane's
-// accumulator registers 8c'..8c'+7 hold.
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int g = (kk >> 2) & 3;
-  const int sg = (g == 1) ? 2 : (g == 2 ? 1 : g);
-  return (kk & ~15) | (sg << 2) | (kk & 3);
+// Chunk swizzles (XOR on the 16-byte chunk index within a row).  K: the 16
+// rows read together by one operand load land on 16 different chunk
+// positions.  V: the 4 rows x 4 chunks read by one transposing load of half
+// a wave land on 16 different chunk positions.
+template <int D>
+__device__ __forceinline__ int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
+
+// Device-only helpers (gfx950 builtins have no host-side meaning).
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// generic pointer into a __shared__ array -> LDS address space (C-style cast:
+// the address-space change is not expressible with the C++ casts)
+__device__ __forceinline__ lds_void* as_lds(const char* p) { return (lds_void*)(const_cast<char*>(p)); }
+__device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<char*>(p)));
 }
 
-template <int D>
-struct TileRegs {
-  u32x4 kr[Smem<D>::KCHUNKS];
-  u32x4 vr[4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, int kv0, int N,
-                                          int tid) {
-  using S = Smem<D>;
-#pragma unroll
-  for (int i = 0; i < S::KCHUNKS; ++i) {
-    const int id = i * NT + tid;
-    const int row = id / (D / 8), col8 = id % (D / 8);
-    const int key = kv0 + row;
-    r.kr[i] = (key < N) ? *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * D + col8 * 8)
-                        : u32x4{0, 0, 0, 0};
-  }
-  if (tid < S::VTHREADS) {
-    const int kgrp = tid % (BC / 4), dchunk = tid / (BC / 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = kv0 + kgrp * 4 + e;
-      r.vr[e] = (key < N) ? *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(key) * D + dchunk * 8)
-                          : u32x4{0, 0, 0, 0};
-    }
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
+// Start the HBM -> LDS copy of K and V rows [kv0, kv0+BC) into one stage.
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, char* stage, int tid) {
-  using S = Smem<D>;
+__device__ __forceinline__ void issue_tile(char* kst, char* vst, const uint16_t* kbase,
+                                           const uint16_t* vbase, int kv0, int N, int wave,
+                                           int lane) {
+  using C = Cfg<D>;
+  const int rows = min(BC, N - kv0);
+  const uint32_t bytes = static_cast<uint32_t>(rows) * C::ROWB;
+  const auto rk = make_rsrc(kbase + static_cast<int64_t>(kv0) * D, bytes);
+  const auto rv = make_rsrc(vbase + static_cast<int64_t>(kv0) * D, bytes);
 #pragma unroll
-  for (int i = 0; i < S::KCHUNKS; ++i) {
-    const int id = i * NT + tid;
-    const int row = id / (D / 8), col8 = id % (D / 8);
-    *reinterpret_cast<u32x4*>(stage + row * S::KROW + col8 * 16) = r.kr[i];
-  }
-  if (tid < S::VTHREADS) {
-    const int kgrp = tid % (BC / 4), dchunk = tid / (BC / 4);
-    char* vt = stage + S::KBYTES + vt_pos(kgrp * 4) * 2;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // channels 2w (low halves) and 2w+1 (high halves) of the 4 keys
-      const uint32_t lo01 = __builtin_amdgcn_perm(r.vr[1][w], r.vr[0][w], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(r.vr[3][w], r.vr[2][w], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(r.vr[1][w], r.vr[0][w], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(r.vr[3][w], r.vr[2][w], 0x07060302u);
-      *reinterpret_cast<u32x2*>(vt + (dchunk * 8 + 2 * w) * S::VROW) = u32x2{lo01, lo23};
-      *reinterpret_cast<u32x2*>(vt + (dchunk * 8 + 2 * w + 1) * S::VROW) = u32x2{hi01, hi23};
-    }
+  for (int b = 0; b < C::BPW; ++b) {
+    const int blk = wave * C::BPW + b;
+    const int row = blk * C::RPB + lane / C::CPR;
+    const int pos = lane % C::CPR;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rk, as_lds(kst + blk * 1024), 16,
+        row * C::ROWB + ((pos ^ kswz<D>(row)) << 4), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, as_lds(vst + blk * 1024), 16,
+        row * C::ROWB + ((pos ^ vswz<D>(row)) << 4), 0, 0, 0);
   }
 }
 
 // v_permlane32_swap with both operands = x: lanes 0..31 get (own, partner),
-// lanes 32..63 get (partner, own), where partner is the lane 32 away; the
-// combination of the pair is therefore the same reduction on every lane.
+// lanes 32..63 get (partner, own), partner being the lane 32 away; combining
+// the pair gives the same two-lane reduction on every lane.
 __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -128,28 +122,135 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+template <int D>
+struct WaveState {
+  bf16x8 qr[D / 16];          // Q^T operand: channels ks*16 + 8h .. +7 of the lane's row
+  f32x16 oacc[D / 32];        // O^T accumulator: 32 channels x 32 rows per block
+  float m;                    // exponent reference (base 2), -inf before the first tile
+  float lsum;                 // this lane half's share of the normaliser
+};
+
+// One key tile for one wave: scores, masks, online softmax, P V.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void tile_step(WaveState<D>& w, const char* kst, const char* vst,
+                                          int kv0, int N, int q0w, int qrow, int j, int h,
+                                          int lane, float c) {
+  using C = Cfg<D>;
+  // ---- S^T = K Q^T (two 32-key blocks) ----
+  f32x16 sacc[BC / 32];
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb) {
+    const int row = kb * 32 + j;
+    const char* krow = kst + row * C::ROWB;
+    const int sw = kswz<D>(row);
+    bf16x8 a[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      a[ks] = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + h) ^ sw) << 4));
+    sacc[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], w.qr[ks], sacc[kb], 0, 0, 0);
+  }
+  // ---- masks: keys past the diagonal (causal), keys past the end ----
+  const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > N);
+  if (need_mask) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool masked = (key >= N) || (CAUSAL && key > qrow);
+        sacc[kb][r] = masked ? -INFINITY : sacc[kb][r];
+      }
+  }
+  // ---- online softmax (base 2), reference raised only when needed ----
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+  const float mt = halves_max(mx) * c;
+  if (__builtin_amdgcn_ballot_w64(mt > w.m + kTau) != 0) {
+    const float mnew = fmaxf(w.m, mt);
+    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(w.m - mnew);
+    w.lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
+    w.m = mnew;
+  }
+  const float mref = (w.m == -INFINITY) ? 0.f : w.m;
+  uint32_t pw[BC / 16][4];
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(fmaf(sacc[kb][r], c, -mref));
+      const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], c, -mref));
+      // the normaliser sums the float32 p (two chains for latency)
+      ls0 += p0;
+      ls1 += p1;
+      // accumulator registers 8c'..8c'+7 of block kb form operand 2kb+c'
+      pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+    }
+  w.lsum += ls0 + ls1;
+  bf16x8 pb[BC / 16];
+#pragma unroll
+  for (int c16 = 0; c16 < BC / 16; ++c16)
+    pb[c16] = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
+  // ---- O^T += V^T P^T: A operand through transposing LDS reads ----
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int b16 = g16 & 1;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int chunk = db * 4 + 2 * b16 + ((r16 & 3) >> 1);
+    const int half8 = (r16 & 1) << 3;
+#pragma unroll
+    for (int c16 = 0; c16 < BC / 16; ++c16) {
+      const int key0 = c16 * 16 + 4 * h + (r16 >> 2);
+      const int key1 = key0 + 8;
+      const v4i16 lo = ds_read_tr16(vst + key0 * C::ROWB + ((chunk ^ vswz<D>(key0)) << 4) + half8);
+      const v4i16 hi = ds_read_tr16(vst + key1 * C::ROWB + ((chunk ^ vswz<D>(key1)) << 4) + half8);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c16], w.oacc[db], 0, 0, 0);
+    }
+  }
+}
+
+#endif  // __HIP_DEVICE_COMPILE__
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(NT, 2)
 attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                       float* __restrict__ lse, int N, int BH, int nqb, float c) {
-  using S = Smem<D>;
-  __shared__ __attribute__((aligned(16))) char smem[S::TOTAL];
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = Cfg<D>;
+  // two stages, each a separate array so the compiler can tell the copy in
+  // flight from the tile being read
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILEB];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int j = lane & 31;        // query column inside the wave's 32
+  const int j = lane & 31;        // query column inside the wave's 32 rows
   const int h = lane >> 5;        // lane half
 
-  // Work item: causal blocks are issued heaviest (last query block) first.
+  // ---- work item: XCD-grouped heads, heaviest causal blocks first ----
+  const int id = static_cast<int>(blockIdx.x);
   int bh, qb;
-  if (CAUSAL) {
-    qb = nqb - 1 - static_cast<int>(blockIdx.x / BH);
-    bh = static_cast<int>(blockIdx.x % BH);
+  if (BH % kXcds == 0) {
+    const int x = id % kXcds, s = id / kXcds, hx = BH / kXcds;
+    if (CAUSAL) { qb = nqb - 1 - s / hx; bh = x + kXcds * (s % hx); }
+    else        { bh = x + kXcds * (s / nqb); qb = s % nqb; }
+  } else if (CAUSAL) {
+    qb = nqb - 1 - id / BH; bh = id % BH;
   } else {
-    bh = static_cast<int>(blockIdx.x / nqb);
-    qb = static_cast<int>(blockIdx.x % nqb);
+    bh = id / nqb; qb = id % nqb;
   }
   const int q0 = qb * BR;
   const int q0w = q0 + wave * BRW;
@@ -158,110 +259,52 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const uint16_t* kbase = k + base;
   const uint16_t* vbase = v + base;
 
-  // Q^T as the B operand: lane (j, h) holds channels ks*16 + 8h .. +7 of row qrow.
-  bf16x8 qr[D / 16];
+  WaveState<D> w;
+  {
+    const int rows = max(0, min(BRW, N - q0w));
+    const auto rq = make_rsrc(q + base + static_cast<int64_t>(min(q0w, N)) * D,
+                              static_cast<uint32_t>(rows) * C::ROWB);
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 x = (qrow < N) ? *reinterpret_cast<const u32x4*>(q + base + static_cast<int64_t>(qrow) * D + ks * 16 + 8 * h)
-                         : u32x4{0, 0, 0, 0};
-    qr[ks] = __builtin_bit_cast(bf16x8, x);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, j * C::ROWB + (ks * 16 + 8 * h) * 2, 0, 0);
+      w.qr[ks] = __builtin_bit_cast(bf16x8, x);
+    }
   }
-
-  f32x16 oacc[D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY, lsum = 0.f;
+  for (int db = 0; db < D / 32; ++db) w.oacc[db] = f32x16{};
+  w.m = -INFINITY;
+  w.lsum = 0.f;
 
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
   const bool wave_live = q0w < N;
 
-  TileRegs<D> regs;
-  load_tile<D>(regs, kbase, vbase, 0, N, tid);
-  store_tile<D>(regs, smem, tid);
+  issue_tile<D>(k0s, v0s, kbase, vbase, 0, N, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int kv0 = t * BC;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile<D>(regs, kbase, vbase, kv0 + BC, N, tid);
-    const char* stage = smem + (t & 1) * S::STAGE;
-
-    const bool wave_needs = wave_live && (!CAUSAL || kv0 <= q0w + BRW - 1);
-    if (wave_needs) {
-      // ---- S^T = K Q^T for the tile's BC keys (two 32-key blocks) ----
-      f32x16 sacc[BC / 32];
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        sacc[kb] = f32x16{};
-        const char* krow = stage + (kb * 32 + j) * S::KROW + 16 * h;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ks * 32);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[ks], sacc[kb], 0, 0, 0);
-        }
-      }
-      // ---- masks: causal diagonal tiles, keys past the sequence end ----
-      const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool masked = (key >= N) || (CAUSAL && key > qrow);
-            if (masked) sacc[kb][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax (base 2) ----
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = halves_max(mx);
-      const float mnew = fmaxf(m, mx * c);
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2(m - mref);
-      m = mnew;
-      float psum = 0.f;
-      uint32_t pw[BC / 16][4];
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(sacc[kb][r], c, -mref));
-          const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], c, -mref));
-          psum += p0 + p1;
-          // accumulator registers 8c'..8c'+7 of block kb form operand 2kb+c'
-          pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-        }
-      }
-      bf16x8 pb[BC / 16];
-#pragma unroll
-      for (int c16 = 0; c16 < BC / 16; ++c16)
-        pb[c16] = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
-      lsum = lsum * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-      // ---- O^T += V^T P^T ----
-      const char* vt = stage + S::KBYTES;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const char* vrow = vt + (db * 32 + j) * S::VROW + 16 * h;
-#pragma unroll
-        for (int c16 = 0; c16 < BC / 16; ++c16) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + c16 * 32);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c16], oacc[db], 0, 0, 0);
-        }
-      }
+  // Two tiles per trip so each stage is a fixed array.
+  for (int t = 0; t < ntiles; t += 2) {
+    {
+      const int kv0 = t * BC;
+      if (t + 1 < ntiles) issue_tile<D>(k1s, v1s, kbase, vbase, kv0 + BC, N, wave, lane);
+      if (wave_live && (!CAUSAL || kv0 <= q0w + BRW - 1))
+        tile_step<D, CAUSAL>(w, k0s, v0s, kv0, N, q0w, qrow, j, h, lane, c);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
-    if (more) store_tile<D>(regs, smem + ((t + 1) & 1) * S::STAGE, tid);
-    __syncthreads();
+    if (t + 1 < ntiles) {
+      const int kv0 = (t + 1) * BC;
+      if (t + 2 < ntiles) issue_tile<D>(k0s, v0s, kbase, vbase, kv0 + BC, N, wave, lane);
+      if (wave_live && (!CAUSAL || kv0 <= q0w + BRW - 1))
+        tile_step<D, CAUSAL>(w, k1s, v1s, kv0, N, q0w, qrow, j, h, lane, c);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: the deferred division, bf16 output, LSE ----
-  const float ltot = halves_sum(lsum);
+  const float ltot = halves_sum(w.lsum);
   if (qrow < N) {
     const float inv = 1.f / ltot;
     uint16_t* orow = o + base + static_cast<int64_t>(qrow) * D;
@@ -270,14 +313,15 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = db * 32 + 8 * g + 4 * h;
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + col) = w;
+        u32x2 wv;
+        wv[0] = pack_bf16x2(w.oacc[db][4 * g + 0] * inv, w.oacc[db][4 * g + 1] * inv);
+        wv[1] = pack_bf16x2(w.oacc[db][4 * g + 2] * inv, w.oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + col) = wv;
       }
     if (lse != nullptr && h == 0)
-      lse[static_cast<int64_t>(bh) * N + qrow] = (m + __log2f(ltot)) * kLn2;
+      lse[static_cast<int64_t>(bh) * N + qrow] = (w.m + __log2f(ltot)) * kLn2;
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 template <int D, bool CAUSAL>
