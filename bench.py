@@ -83,6 +83,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal_16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of 1 GiB per step (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -93,6 +95,16 @@ def main() -> int:
     import torch
     import exact_attention_127_amd as A
     from seeded_inputs import WORKLOADS, make_inputs
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2,
+                          "launches": args.warmup + args.steps}))
+        return 0
 
     w = WORKLOADS[args.workload]
     if w.dtype != "bf16":
@@ -111,6 +123,11 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # keep warming until the clocks have settled (about one second of work)
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 1.0:
+        step()
+        torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()

@@ -22,26 +22,33 @@
 //    its A operand (V^T) comes from row-major V in LDS through
 //    ds_read_b64_tr_b16, which hands each lane four keys of one channel, read
 //    in exactly the key order the accumulator registers hold.
+//  * Each wave software-pipelines its tiles: while the matrix cores compute
+//    the scores of tile t+1, the vector ALUs run the exponentials of tile t;
+//    while they compute P V of tile t, the vector ALUs take the row maximum
+//    of tile t+1.  The two streams are interleaved instruction by instruction
+//    (scheduling groups), which is what lets MFMA and VALU work overlap
+//    inside one wave.
 //  * K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16
-//    bytes per lane, no register staging), double-buffered so tile t+1 is in
-//    flight while tile t is computed; one barrier per tile.  Out-of-range
-//    rows of the last tile read as zero (buffer bounds).  16-byte chunks are
-//    XOR-swizzled per row so the matrix-operand reads hit distinct banks.
+//    bytes per lane, no register staging) in two-slot rings: K of tile t+2
+//    and V of tile t+1 are copied while tile t is processed; one barrier per
+//    tile.  Out-of-range rows read as zero (buffer bounds).  16-byte chunks
+//    are XOR-swizzled per row so the operand reads hit distinct LDS banks.
 //  * The running maximum used as the exponent reference is only raised when
-//    some row's tile maximum exceeds it by more than 2^kTau (base 2); p then
+//    some row's tile maximum exceeds it by more than kTau (base 2); p then
 //    stays <= 2^kTau, the normaliser and the partial output carry the same
 //    reference, and the single division at the end cancels it exactly.  Most
 //    tiles of a long row therefore skip the rescale of the partial output.
-//  * Work items are grouped by XCD (dispatch is round-robin over the 8 XCDs)
-//    so the query blocks of one head share one L2, heaviest causal blocks
-//    first.
+//  * Two workgroups share a CU (one wave of each per SIMD), so one hides the
+//    other's barrier and copy waits.  Work items are grouped by XCD
+//    (dispatch is round-robin over the 8 XCDs) so the query blocks of one
+//    head share one L2, heaviest causal blocks first.
 #include "common.h"
 #include "launch.h"
 
 namespace attn127 {
 namespace {
 
-constexpr int NW = 4;            // waves per workgroup
+constexpr int NW = 4;            // waves per workgroup (one per SIMD)
 constexpr int BRW = 32;          // query rows per wave
 constexpr int BR = NW * BRW;     // query rows per workgroup
 constexpr int BC = 64;           // keys per tile
@@ -53,10 +60,10 @@ template <int D>
 struct Cfg {
   static constexpr int ROWB = D * 2;           // bytes per K/V row
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int RPB = 1024 / ROWB;      // rows per 1 KB load block
+  static constexpr int RPB = 1024 / ROWB;      // rows per 1 KB copy block
   static constexpr int TILEB = BC * ROWB;      // bytes of one K (or V) tile
   static constexpr int BLK = TILEB / 1024;     // 1 KB blocks per tile
-  static constexpr int BPW = BLK / NW;         // blocks per wave per tile
+  static constexpr int BPW = BLK / NW;         // blocks of one tile copied per wave
   static_assert(BPW * NW == BLK, "tile must split evenly over the waves");
 };
 
@@ -69,11 +76,15 @@ __device__ __forceinline__ int kswz(int row) { return D == 128 ? (row & 15) : ((
 template <int D>
 __device__ __forceinline__ int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
+// Scheduling-group masks (LLVM AMDGPU sched_group_barrier).
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100, kSgTrans = 0x400;
+
 // Device-only helpers (gfx950 builtins have no host-side meaning).
 #if defined(__HIP_DEVICE_COMPILE__)
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // generic pointer into a __shared__ array -> LDS address space (C-style cast:
 // the address-space change is not expressible with the C++ casts)
@@ -82,32 +93,52 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<char*>(p)));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+// Buffer descriptor for `bytes` bytes from `base`: reads past the end return 0.
+__device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int>(static_cast<uint32_t>(a)), static_cast<int>(static_cast<uint32_t>(a >> 32)),
+               static_cast<int>(bytes), 0x00020000};
 }
 
-// Start the HBM -> LDS copy of K and V rows [kv0, kv0+BC) into one stage.
-template <int D>
-__device__ __forceinline__ void issue_tile(char* kst, char* vst, const uint16_t* kbase,
-                                           const uint16_t* vbase, int kv0, int N, int wave,
-                                           int lane) {
+// One 16-byte-per-lane HBM -> LDS copy: lane i's 16 bytes land at
+// lds_block + 16*i.  Issued as inline assembly so the compiler does not
+// serialise it against unrelated LDS reads; completion is tracked by the
+// explicit vmcnt waits of the tile loop.
+__device__ __forceinline__ void dma16(const i32x4& desc, const char* lds_block, int voffset) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(as_lds(lds_block))));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m), "v"(voffset), "s"(desc) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Copy rows [kv0, kv0+BC) of one (b,h) slice of K or V into an LDS tile;
+// each wave copies BPW one-kilobyte blocks.
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_copy(char* dst, const uint16_t* src, int kv0, int N,
+                                           int wave, int lane) {
   using C = Cfg<D>;
   const int rows = min(BC, N - kv0);
-  const uint32_t bytes = static_cast<uint32_t>(rows) * C::ROWB;
-  const auto rk = make_rsrc(kbase + static_cast<int64_t>(kv0) * D, bytes);
-  const auto rv = make_rsrc(vbase + static_cast<int64_t>(kv0) * D, bytes);
+  const i32x4 desc = buffer_desc(src + static_cast<int64_t>(kv0) * D,
+                                 static_cast<uint32_t>(rows) * C::ROWB);
 #pragma unroll
   for (int b = 0; b < C::BPW; ++b) {
     const int blk = wave * C::BPW + b;
     const int row = blk * C::RPB + lane / C::CPR;
     const int pos = lane % C::CPR;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rk, as_lds(kst + blk * 1024), 16,
-        row * C::ROWB + ((pos ^ kswz<D>(row)) << 4), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rv, as_lds(vst + blk * 1024), 16,
-        row * C::ROWB + ((pos ^ vswz<D>(row)) << 4), 0, 0, 0);
+    const int sw = IS_V ? vswz<D>(row) : kswz<D>(row);
+    dma16(desc, dst + blk * 1024, row * C::ROWB + ((pos ^ sw) << 4));
   }
+}
+
+// Wait until at most n of this wave's vector-memory operations are in
+// flight (s_waitcnt vmcnt(n); the expcnt and lgkmcnt fields left at maximum).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
 }
 
 // v_permlane32_swap with both operands = x: lanes 0..31 get (own, partner),
@@ -130,47 +161,72 @@ struct WaveState {
   float lsum;                 // this lane half's share of the normaliser
 };
 
-// One key tile for one wave: scores, masks, online softmax, P V.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void tile_step(WaveState<D>& w, const char* kst, const char* vst,
-                                          int kv0, int N, int q0w, int qrow, int j, int h,
-                                          int lane, float c) {
-  using C = Cfg<D>;
-  // ---- S^T = K Q^T (two 32-key blocks) ----
-  f32x16 sacc[BC / 32];
+// Lane-constant parts of the LDS operand addresses.  K operand reads: one
+// byte offset per 16-channel step (the row swizzle makes them irregular; the
+// second 32-key block adds a constant).  V transposing reads: one base per
+// 32-channel block; keys enter as compile-time offsets because the V swizzle
+// depends only on key bits that are the same for all of a lane's reads.
+template <int D>
+struct LaneAddr {
+  int kofs[D / 16];
+  int vbase[D / 32];
+  __device__ __forceinline__ LaneAddr(int j, int h, int lane) {
+    using C = Cfg<D>;
+    const int ksw = kswz<D>(j);   // rows j and 32+j share the swizzle
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kofs[ks] = j * C::ROWB + (((2 * ks + h) ^ ksw) << 4);
+    const int g16 = lane >> 4, r16 = lane & 15, b16 = g16 & 1;
+    const int key0 = 4 * h + (r16 >> 2);                 // key of the first read in chunk 0
+    const int vs = vswz<D>(key0);                         // equals vswz of every key0 + 8i
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int chunk = db * 4 + 2 * b16 + ((r16 & 3) >> 1);
+      vbase[db] = key0 * C::ROWB + ((chunk ^ vs) << 4) + ((r16 & 1) << 3);
+    }
+  }
+};
+
+// S^T = K Q^T for one tile (two 32-key blocks), K from LDS.
+template <int D>
+__device__ __forceinline__ void scores(f32x16 (&sacc)[BC / 32], const WaveState<D>& w,
+                                       const LaneAddr<D>& la, const char* kst, int h) {
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb) {
-    const int row = kb * 32 + j;
-    const char* krow = kst + row * C::ROWB;
-    const int sw = kswz<D>(row);
-    bf16x8 a[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      a[ks] = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + h) ^ sw) << 4));
     sacc[kb] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], w.qr[ks], sacc[kb], 0, 0, 0);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * Cfg<D>::ROWB + la.kofs[ks]);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qr[ks], sacc[kb], 0, 0, 0);
+    }
   }
-  // ---- masks: keys past the diagonal (causal), keys past the end ----
-  const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > N);
-  if (need_mask) {
+}
+
+// Keys past the diagonal (causal) or past the sequence end -> -inf.
+template <bool CAUSAL>
+__device__ __forceinline__ void apply_mask(f32x16 (&sacc)[BC / 32], int kv0, int N, int qrow, int h) {
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
+  for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool masked = (key >= N) || (CAUSAL && key > qrow);
-        sacc[kb][r] = masked ? -INFINITY : sacc[kb][r];
-      }
-  }
-  // ---- online softmax (base 2), reference raised only when needed ----
+    for (int r = 0; r < 16; ++r) {
+      const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const bool masked = (key >= N) || (CAUSAL && key > qrow);
+      sacc[kb][r] = masked ? -INFINITY : sacc[kb][r];
+    }
+}
+
+__device__ __forceinline__ float tile_max(const f32x16 (&sacc)[BC / 32]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-  const float mt = halves_max(mx) * c;
+  return mx;
+}
+
+// Raise the exponent reference if some row's tile maximum (already scaled
+// by c, both lane halves combined) exceeds it by more than kTau.
+template <int D>
+__device__ __forceinline__ void update_reference(WaveState<D>& w, float mt) {
   if (__builtin_amdgcn_ballot_w64(mt > w.m + kTau) != 0) {
     const float mnew = fmaxf(w.m, mt);
     const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(w.m - mnew);
@@ -179,6 +235,14 @@ __device__ __forceinline__ void tile_step(WaveState<D>& w, const char* kst, cons
     for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
     w.m = mnew;
   }
+}
+
+// p = exp2(s*c - m) for one tile: the float32 p go into the normaliser, the
+// bf16-rounded p into the B operand of P V (16 keys per entry, in the
+// accumulator's key order).
+template <int D>
+__device__ __forceinline__ void softmax_tile(WaveState<D>& w, bf16x8 (&pb)[BC / 16],
+                                             const f32x16 (&sacc)[BC / 32], float c) {
   const float mref = (w.m == -INFINITY) ? 0.f : w.m;
   uint32_t pw[BC / 16][4];
   float ls0 = 0.f, ls1 = 0.f;
@@ -188,36 +252,75 @@ __device__ __forceinline__ void tile_step(WaveState<D>& w, const char* kst, cons
     for (int r = 0; r < 16; r += 2) {
       const float p0 = fast_exp2(fmaf(sacc[kb][r], c, -mref));
       const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], c, -mref));
-      // the normaliser sums the float32 p (two chains for latency)
       ls0 += p0;
       ls1 += p1;
       // accumulator registers 8c'..8c'+7 of block kb form operand 2kb+c'
       pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
     }
   w.lsum += ls0 + ls1;
-  bf16x8 pb[BC / 16];
 #pragma unroll
   for (int c16 = 0; c16 < BC / 16; ++c16)
     pb[c16] = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
-  // ---- O^T += V^T P^T: A operand through transposing LDS reads ----
-  const int g16 = lane >> 4, r16 = lane & 15;
-  const int b16 = g16 & 1;
+}
+
+// O^T += V^T P^T for one tile, V^T through transposing LDS reads.
+template <int D>
+__device__ __forceinline__ void pv_tile(WaveState<D>& w, const bf16x8 (&pb)[BC / 16],
+                                        const LaneAddr<D>& la, const char* vst) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    const int chunk = db * 4 + 2 * b16 + ((r16 & 3) >> 1);
-    const int half8 = (r16 & 1) << 3;
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int c16 = 0; c16 < BC / 16; ++c16) {
-      const int key0 = c16 * 16 + 4 * h + (r16 >> 2);
-      const int key1 = key0 + 8;
-      const v4i16 lo = ds_read_tr16(vst + key0 * C::ROWB + ((chunk ^ vswz<D>(key0)) << 4) + half8);
-      const v4i16 hi = ds_read_tr16(vst + key1 * C::ROWB + ((chunk ^ vswz<D>(key1)) << 4) + half8);
+      const v4i16 lo = ds_read_tr16(vst + la.vbase[db] + (c16 * 16) * Cfg<D>::ROWB);
+      const v4i16 hi = ds_read_tr16(vst + la.vbase[db] + (c16 * 16 + 8) * Cfg<D>::ROWB);
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c16], w.oacc[db], 0, 0, 0);
     }
-  }
 }
 
+// Phase A of a pipelined tile: scores of the next tile on the matrix cores,
+// interleaved with the exponentials of the current tile on the vector ALUs.
+template <int D>
+__device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32],
+                                        bf16x8 (&pb)[BC / 16], const f32x16 (&scur)[BC / 32],
+                                        const LaneAddr<D>& la, const char* kst_next, int h,
+                                        float c) {
+  __builtin_amdgcn_sched_barrier(0);
+  scores<D>(snext, w, la, kst_next, h);
+  softmax_tile<D>(w, pb, scur, c);
+  constexpr int nm = (BC / 32) * (D / 16);     // MFMAs in the block
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+#pragma unroll
+  for (int i = 0; i < nm; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if (i + 4 < nm) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgTrans, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, 5, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Phase B: P V of the current tile on the matrix cores, interleaved with the
+// (masked) row maximum of the next tile on the vector ALUs.
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32],
+                                         const bf16x8 (&pb)[BC / 16], const LaneAddr<D>& la,
+                                         const char* vst, int kv0n, int N, int qrow, int h) {
+  __builtin_amdgcn_sched_barrier(0);
+  pv_tile<D>(w, pb, la, vst);
+  if (MASK) apply_mask<CAUSAL>(snext, kv0n, N, qrow, h);
+  const float mx = tile_max(snext);
+  constexpr int nm = (D / 32) * (BC / 16);
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+#pragma unroll
+  for (int i = 0; i < nm; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if (i + 2 < nm) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, MASK ? 6 : 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return mx;
+}
 #endif  // __HIP_DEVICE_COMPILE__
 
 template <int D, bool CAUSAL>
@@ -227,12 +330,10 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       float* __restrict__ lse, int N, int BH, int nqb, float c) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = Cfg<D>;
-  // two stages, each a separate array so the compiler can tell the copy in
-  // flight from the tile being read
-  __shared__ __attribute__((aligned(1024))) char k0s[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v0s[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char k1s[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v1s[C::TILEB];
+  // two-slot rings for K and V tiles
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILEB];
+  char* const kring = smem;
+  char* const vring = smem + 2 * C::TILEB;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -260,47 +361,73 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const uint16_t* vbase = v + base;
 
   WaveState<D> w;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) w.oacc[db] = f32x16{};
+  w.m = -INFINITY;
+  w.lsum = 0.f;
+  const LaneAddr<D> la(j, h, lane);
+
+  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+  // last tile this wave needs (-1: the wave's rows are all past the end)
+  int last = -1;
+  if (q0w < N) last = CAUSAL ? min(ntiles - 1, (q0w + BRW - 1) / BC) : ntiles - 1;
+
+  // ---- prologue: K0, V0, K1 and Q in flight; scores of tile 0 ----
+  issue_copy<D, false>(kring, kbase, 0, N, wave, lane);
+  issue_copy<D, true>(vring, vbase, 0, N, wave, lane);
+  if (ntiles > 1) issue_copy<D, false>(kring + C::TILEB, kbase, BC, N, wave, lane);
   {
     const int rows = max(0, min(BRW, N - q0w));
-    const auto rq = make_rsrc(q + base + static_cast<int64_t>(min(q0w, N)) * D,
-                              static_cast<uint32_t>(rows) * C::ROWB);
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q + base + static_cast<int64_t>(min(q0w, N)) * D), 0,
+        static_cast<int>(rows * C::ROWB), 0x00020000);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, j * C::ROWB + (ks * 16 + 8 * h) * 2, 0, 0);
       w.qr[ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) w.oacc[db] = f32x16{};
-  w.m = -INFINITY;
-  w.lsum = 0.f;
-
-  const int kend = CAUSAL ? min(N, q0 + BR) : N;
-  const int ntiles = (kend + BC - 1) / BC;
-  const bool wave_live = q0w < N;
-
-  issue_tile<D>(k0s, v0s, kbase, vbase, 0, N, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_vmcnt<0>();
   __syncthreads();
 
-  // Two tiles per trip so each stage is a fixed array.
+  f32x16 sa[BC / 32], sb[BC / 32];   // scores of the current and the next tile
+  bf16x8 pb[BC / 16];
+  if (last >= 0) {
+    scores<D>(sa, w, la, kring, h);
+    if ((CAUSAL && BC - 1 > q0w) || BC > N) apply_mask<CAUSAL>(sa, 0, N, qrow, h);
+    update_reference<D>(w, halves_max(tile_max(sa)) * c);
+  }
+  __syncthreads();   // every wave is done with K0 before its slot is refilled
+
+  // ---- main loop: at the top of iteration t the scores of tile t are in
+  // registers (masked, reference updated), K of tile t+1 and V of tile t are
+  // in LDS.  Iteration t copies V of t+1 and K of t+2.
+  // The score buffers alternate roles each tile; two tiles per trip keep
+  // that choice static.
+  auto iteration = [&](int t, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32]) {
+    const char* kst_next = kring + ((t + 1) & 1) * C::TILEB;
+    const char* vst = vring + (t & 1) * C::TILEB;
+    if (t + 1 < ntiles) issue_copy<D, true>(vring + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave, lane);
+    if (t + 2 < ntiles) issue_copy<D, false>(kring + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
+    if (t < last) {
+      const int kv0n = (t + 1) * BC;
+      phase_a<D>(w, snext, pb, scur, la, kst_next, h, c);
+      const bool mask_next = (CAUSAL && kv0n + BC - 1 > q0w) || (kv0n + BC > N);
+      float mx;
+      if (mask_next) mx = phase_b<D, CAUSAL, true>(w, snext, pb, la, vst, kv0n, N, qrow, h);
+      else           mx = phase_b<D, CAUSAL, false>(w, snext, pb, la, vst, kv0n, N, qrow, h);
+      update_reference<D>(w, halves_max(mx) * c);
+    } else if (t == last) {
+      softmax_tile<D>(w, pb, scur, c);
+      pv_tile<D>(w, pb, la, vst);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  };
   for (int t = 0; t < ntiles; t += 2) {
-    {
-      const int kv0 = t * BC;
-      if (t + 1 < ntiles) issue_tile<D>(k1s, v1s, kbase, vbase, kv0 + BC, N, wave, lane);
-      if (wave_live && (!CAUSAL || kv0 <= q0w + BRW - 1))
-        tile_step<D, CAUSAL>(w, k0s, v0s, kv0, N, q0w, qrow, j, h, lane, c);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-    if (t + 1 < ntiles) {
-      const int kv0 = (t + 1) * BC;
-      if (t + 2 < ntiles) issue_tile<D>(k0s, v0s, kbase, vbase, kv0 + BC, N, wave, lane);
-      if (wave_live && (!CAUSAL || kv0 <= q0w + BRW - 1))
-        tile_step<D, CAUSAL>(w, k1s, v1s, kv0, N, q0w, qrow, j, h, lane, c);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+    iteration(t, sa, sb);
+    if (t + 1 < ntiles) iteration(t + 1, sb, sa);
   }
 
   // ---- epilogue: the deferred division, bf16 output, LSE ----
