@@ -1,8 +1,463 @@
-// fp8 (e4m3) path: placeholder until the kernels land.
+// fp8 (OCP e4m3) path: block quantisation with incoherent processing, and
+// the fused attention forward on fp8 matrix cores (gfx950).
+//
+// Page "FlashAttention scaling, multi-GPU training and weight quantization",
+// section 1, the FP8 bullet: low-precision matrix units double the matmul
+// rate, and two measures keep outliers from ruining accuracy -- an
+// independent scale for each small tile (block quantisation) and
+// multiplying Q and K by a random orthogonal matrix first (incoherent
+// processing), which leaves Q K^T unchanged.
+//
+// attn_fp8_prepare: per (tensor, batch*head, tile of 128 tokens) one
+// workgroup loads the tile, rotates it (Q and K: x R in float32), takes the
+// tile's largest magnitude, sets s = amax/448 and writes e4m3(x/s) with
+// nearest-even rounding and saturation.
+//
+// attn_fwd_fp8: the bf16 kernel's structure (transposed scores, in-register
+// online softmax, deferred normalisation, HBM -> LDS copies) with the scores
+// on v_mfma_f32_32x32x64_f8f6f4: S^T = K^ Q^^T, the tile scales of Q and K
+// folded into the exponent's multiplier.  The second product stays on bf16
+// matrix cores: each wave converts the e4m3 V codes it copied into a bf16 V
+// tile (exact), and the V tile's scale rides on P (p * s_v rounded to bf16).
+// Rounding P to e4m3 instead would cost up to 2^-4 of every weight, which
+// with the x40 outlier channels of V exceeds the accuracy bound; bf16 P costs
+// 2^-9.
+#include <math.h>
+
 #include "common.h"
 #include "launch.h"
+#if defined(__HIP_DEVICE_COMPILE__)
+#include "device_util.h"
+#endif
 
 namespace attn127 {
-hipError_t launch_fp8_prepare(const Fp8PrepArgs&) { return hipErrorNotSupported; }
-hipError_t launch_fp8_fwd(const Fp8Args&) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kTile8 = 128;          // tokens per quantisation tile
+constexpr float kE4m3Max = 448.0f;
+
+// ---------------------------------------------------------------------------
+// prepare
+// ---------------------------------------------------------------------------
+constexpr int kPrepThreads = 256;
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// Nearest e4m3 (E4M3FN) code of x: ties to even, |x| >= 448 saturates to
+// 448, NaN -> 0x7F.  Normal range: fp32 mantissa rounded to 3 bits at bit
+// 20, exponent rebiased 127 -> 7; below 2^-6 the spacing is 2^-9.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  if (x != x) return 0x7Fu;
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a >= kE4m3Max) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // 0..8 (8 = 2^-6)
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    code = (b >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+#endif
+
+template <int D>
+__global__ void __launch_bounds__(kPrepThreads)
+fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                   const float* __restrict__ v, const float* __restrict__ R,
+                   uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, uint8_t* __restrict__ v8,
+                   float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv,
+                   int N, int BH, int ntq) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int TP = kTile8 + 1;                 // padded token stride of the transposed tile
+  __shared__ float xt[D * TP];                   // x^T: xt[c*TP + token]
+  __shared__ float rs[D * D];                    // R row-major
+  __shared__ float red[kPrepThreads / 64];
+
+  const int tid = threadIdx.x;
+  int id = static_cast<int>(blockIdx.x);
+  const int tensor = id / (BH * ntq);
+  id -= tensor * BH * ntq;
+  const int bh = id / ntq, tile = id % ntq;
+  const float* src = tensor == 0 ? q : (tensor == 1 ? k : v);
+  uint8_t* dst = tensor == 0 ? q8 : (tensor == 1 ? k8 : v8);
+  float* scale_out = tensor == 0 ? sq : (tensor == 1 ? sk : sv);
+  const bool rotate = tensor < 2;
+  const int t0 = tile * kTile8;
+  const int rows = min(kTile8, N - t0);
+  const int64_t off = (static_cast<int64_t>(bh) * N + t0) * D;
+
+  for (int e = tid; e < kTile8 * D; e += kPrepThreads) {
+    const int r = e / D, col = e % D;
+    xt[col * TP + r] = (r < rows) ? src[off + static_cast<int64_t>(r) * D + col] : 0.f;
+  }
+  if (rotate)
+    for (int e = tid; e < D * D; e += kPrepThreads) rs[e] = R[e];
+  __syncthreads();
+
+  // each thread: TT tokens x 8 channels
+  constexpr int CG = D / 8;                      // channel groups
+  constexpr int TT = kTile8 * CG / kPrepThreads; // tokens per thread (8 for D=128, 4 for D=64)
+  const int cc = (tid % CG) * 8;
+  const int tt = (tid / CG) * TT;
+  float y[TT][8];
+  if (rotate) {
+#pragma unroll
+    for (int r = 0; r < TT; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[r][c] = 0.f;
+    for (int i = 0; i < D; ++i) {
+      float a[TT], b[8];
+#pragma unroll
+      for (int r = 0; r < TT; ++r) a[r] = xt[i * TP + tt + r];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) b[c] = rs[i * D + cc + c];
+#pragma unroll
+      for (int r = 0; r < TT; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[r][c] = fmaf(a[r], b[c], y[r][c]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < TT; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[r][c] = xt[(cc + c) * TP + tt + r];
+  }
+  // amax over the tile (padding rows are zero)
+  float am = 0.f;
+#pragma unroll
+  for (int r = 0; r < TT; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(y[r][c]));
+  for (int s = 32; s > 0; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
+  if ((tid & 63) == 0) red[tid >> 6] = am;
+  __syncthreads();
+  am = red[0];
+#pragma unroll
+  for (int w = 1; w < kPrepThreads / 64; ++w) am = fmaxf(am, red[w]);
+  const float s = am > 0.f ? am / kE4m3Max : 1.f;
+  if (tid == 0) scale_out[static_cast<int64_t>(bh) * ntq + tile] = s;
+#pragma unroll
+  for (int r = 0; r < TT; ++r) {
+    if (tt + r >= rows) break;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) lo |= e4m3_encode(y[r][c] / s) << (8 * c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) hi |= e4m3_encode(y[r][c + 4] / s) << (8 * c);
+    *reinterpret_cast<u32x2*>(dst + off + static_cast<int64_t>(tt + r) * D + cc) = u32x2{lo, hi};
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+constexpr int NW8 = 4;               // waves per workgroup
+constexpr int BR8 = NW8 * 32;        // query rows per workgroup (one quantisation tile)
+constexpr int BC8 = 64;              // keys per tile (half a quantisation tile)
+constexpr int NT8 = NW8 * 64;
+constexpr float kTau8 = 8.0f;        // p <= 2^kTau8 (exponent reference raised lazily)
+static_assert(BR8 == kTile8, "a workgroup's rows share one Q scale");
+
+template <int D>
+struct Cfg8 {
+  static constexpr int ROWB = D;               // bytes per fp8 K/V row
+  static constexpr int ROWB16 = 2 * D;         // bytes per bf16 V row
+  static constexpr int CPR = D / 16;           // 16-byte chunks per fp8 row
+  static constexpr int RPB = 1024 / ROWB;      // fp8 rows per 1 KB copy block
+  static constexpr int TILEB = BC8 * ROWB;     // fp8 tile
+  static constexpr int TILEB16 = BC8 * ROWB16; // bf16 V tile
+  static constexpr int BLK = TILEB / 1024;
+  static constexpr int BPW = BLK / NW8;
+  static_assert(BPW * NW8 == BLK, "tile must split evenly over the waves");
+};
+
+// fp8 rows: chunk swizzle spreading the rows that one K operand read touches
+// over distinct LDS bank groups (two rows share a 256-byte bank window at
+// D=128, four at D=64).
+template <int D>
+__device__ __forceinline__ int swz8(int row) { return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
+// bf16 V rows: the swizzle under which the 4 rows x 4 chunks of one
+// transposing read of half a wave hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz16(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
+
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int D>
+__device__ __forceinline__ void issue_copy8(char* dst, const uint8_t* src, int kv0, int N, int wave, int lane) {
+  using C = Cfg8<D>;
+  const int rows = min(BC8, N - kv0);
+  const i32x4 desc = buffer_desc(src + static_cast<int64_t>(kv0) * D, static_cast<uint32_t>(rows) * C::ROWB);
+#pragma unroll
+  for (int b = 0; b < C::BPW; ++b) {
+    const int blk = wave * C::BPW + b;
+    const int row = blk * C::RPB + lane / C::CPR;
+    const int pos = lane % C::CPR;
+    dma16(desc, dst + blk * 1024, row * C::ROWB + ((pos ^ swz8<D>(row)) << 4));
+  }
+}
+
+// The blocks of a V tile this wave copied: e4m3 codes -> bf16 (exact), into
+// the bf16 tile.  Lane i's 16 codes are channels 16c..16c+15 of one row.
+template <int D>
+__device__ __forceinline__ void convert_v(char* dst16, const char* src8, int wave, int lane) {
+  using C = Cfg8<D>;
+#pragma unroll
+  for (int b = 0; b < C::BPW; ++b) {
+    const int blk = wave * C::BPW + b;
+    const int row = blk * C::RPB + lane / C::CPR;
+    const int c = (lane % C::CPR) ^ swz8<D>(row);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(src8 + blk * 1024 + lane * 16);
+    u32x4 lo, hi;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
+      lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
+      hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], 1.0f, false));
+      hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], 1.0f, true));
+    }
+    char* r16 = dst16 + row * C::ROWB16;
+    *reinterpret_cast<u32x4*>(r16 + (((2 * c) ^ swz16<D>(row)) << 4)) = lo;
+    *reinterpret_cast<u32x4*>(r16 + (((2 * c + 1) ^ swz16<D>(row)) << 4)) = hi;
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // operand formats 0/0 = e4m3; block scales 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+#endif
+
+// Scores on fp8 MFMA; P V on bf16 MFMA with V^ converted exactly to bf16 and
+// the V tile scale carried by P (p * s_v rounded to bf16: the same relative
+// rounding as the bf16 kernel's P, where e4m3 P would lose up to 2^-4 of
+// each weight).
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(NT8, 2)
+attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
+                const uint8_t* __restrict__ v8, const float* __restrict__ sq,
+                const float* __restrict__ sk, const float* __restrict__ sv,
+                uint16_t* __restrict__ o, float* __restrict__ lse, int N, int BH, int nqb,
+                int ntq, float c0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = Cfg8<D>;
+  __shared__ __attribute__((aligned(1024))) char kring[2 * C::TILEB];     // fp8 K, two slots
+  __shared__ __attribute__((aligned(1024))) char vstage[C::TILEB];        // fp8 V landing area
+  __shared__ __attribute__((aligned(1024))) char vring[2 * C::TILEB16];   // bf16 V, two slots
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+
+  const int id = static_cast<int>(blockIdx.x);
+  int bh, qbk;
+  if (CAUSAL) { qbk = nqb - 1 - id / BH; bh = id % BH; }
+  else        { bh = id / nqb; qbk = id % nqb; }
+  const int q0 = qbk * BR8;
+  const int q0w = q0 + wave * 32;
+  const int qrow = q0w + j;
+  const int64_t base = static_cast<int64_t>(bh) * N * D;
+  const uint8_t* kbase = k8 + base;
+  const uint8_t* vbase = v8 + base;
+  const float* skh = sk + static_cast<int64_t>(bh) * ntq;
+  const float* svh = sv + static_cast<int64_t>(bh) * ntq;
+  // exponent multiplier without the key tile's scale: s_q * scale * log2(e)
+  const float cq = c0 * sq[static_cast<int64_t>(bh) * ntq + q0 / kTile8];
+
+  const int kend = CAUSAL ? min(N, q0 + BR8) : N;
+  const int ntiles = (kend + BC8 - 1) / BC8;
+  int last = -1;
+  if (q0w < N) last = CAUSAL ? min(ntiles - 1, (q0w + 31) / BC8) : ntiles - 1;
+
+  issue_copy8<D>(kring, kbase, 0, N, wave, lane);
+  issue_copy8<D>(vstage, vbase, 0, N, wave, lane);
+
+  // Q^ as the B operand: k-step ks holds channels ks*64 + 32h .. +31
+  i32x8 qr[D / 64];
+  {
+    const int rows = max(0, min(32, N - q0w));
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(q8 + base + static_cast<int64_t>(min(q0w, N)) * D), 0, rows * D, 0x00020000);
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rq, j * D + ks * 64 + 32 * h, 0, 0);
+      const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rq, j * D + ks * 64 + 32 * h + 16, 0, 0);
+      qr[ks] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                     static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+    }
+  }
+  wait_vmcnt<0>();
+  convert_v<D>(vring, vstage, wave, lane);     // this wave's own copied blocks
+  __syncthreads();
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;
+
+  // lane-constant LDS offsets
+  const int ksw = swz8<D>(j);                     // rows j and 32+j share it
+  const int r16 = lane & 15, b16 = (lane >> 4) & 1;
+  const int vkey0 = 4 * h + (r16 >> 2);
+  const int vs16 = swz16<D>(vkey0);               // equals swz16 of every vkey0 + 8i
+  int vbase16[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int chunk = db * 4 + 2 * b16 + ((r16 & 3) >> 1);
+    vbase16[db] = vkey0 * C::ROWB16 + ((chunk ^ vs16) << 4) + ((r16 & 1) << 3);
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kv0 = t * BC8;
+    const char* kst = kring + (t & 1) * C::TILEB;
+    const char* vst = vring + (t & 1) * C::TILEB16;
+    if (t + 1 < ntiles) {
+      issue_copy8<D>(kring + ((t + 1) & 1) * C::TILEB, kbase, kv0 + BC8, N, wave, lane);
+      issue_copy8<D>(vstage, vbase, kv0 + BC8, N, wave, lane);
+    }
+    if (t <= last) {
+      // ---- S^T = K^ Q^^T, two 32-key blocks ----
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+        const char* krow = kst + (kb * 32 + j) * C::ROWB;
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks) {
+          const int c0i = 4 * ks + 2 * h;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + ((c0i ^ ksw) << 4));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + (((c0i + 1) ^ ksw) << 4));
+          const i32x8 a = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                                static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+          sacc[kb] = mfma_fp8(a, qr[ks], sacc[kb]);
+        }
+      }
+      // ---- masks ----
+      if ((CAUSAL && kv0 + BC8 - 1 > q0w) || kv0 + BC8 > N) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const bool masked = (key >= N) || (CAUSAL && key > qrow);
+            sacc[kb][r] = masked ? -INFINITY : sacc[kb][r];
+          }
+      }
+      // ---- online softmax; the key tile's scale enters the multiplier ----
+      const float ct = cq * skh[kv0 / kTile8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      const float mt = halves_max(mx) * ct;
+      if (__builtin_amdgcn_ballot_w64(mt > m + kTau8) != 0) {
+        const float mnew = fmaxf(m, mt);
+        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      }
+      // operand p' = p * s_v = exp2(s*ct - m + log2 s_v); the normaliser
+      // takes sum(p') / s_v
+      const float svt = svh[kv0 / kTile8];
+      const float mref = ((m == -INFINITY) ? 0.f : m) - __log2f(svt);
+      uint32_t pw[4][4];
+      float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(sacc[kb][r], ct, -mref));
+          const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], ct, -mref));
+          ls0 += p0;
+          ls1 += p1;
+          pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+        }
+      lsum += (ls0 + ls1) / svt;
+      // ---- O^T += V^T P'^T (bf16) ----
+#pragma unroll
+      for (int c16 = 0; c16 < 4; ++c16) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const v4i16 lo = ds_read_tr16(vst + vbase16[db] + (c16 * 16) * C::ROWB16);
+          const v4i16 hi = ds_read_tr16(vst + vbase16[db] + (c16 * 16 + 8) * C::ROWB16);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < ntiles) {
+      // this wave's copies of tile t+1 have landed: publish its K, convert
+      // its V blocks into the free bf16 slot (tile t-1's, read before the
+      // previous barrier)
+      wait_vmcnt<0>();
+      convert_v<D>(vring + ((t + 1) & 1) * C::TILEB16, vstage, wave, lane);
+    }
+    __syncthreads();
+  }
+
+  const float ltot = halves_sum(lsum);
+  if (qrow < N) {
+    const float inv = 1.f / ltot;
+    uint16_t* orow = o + base + static_cast<int64_t>(qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = db * 32 + 8 * g + 4 * h;
+        u32x2 wv;
+        wv[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+        wv[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + col) = wv;
+      }
+    if (lse != nullptr && h == 0)
+      lse[static_cast<int64_t>(bh) * N + qrow] = (m + __log2f(ltot)) * kLn2;
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int D>
+hipError_t prep_one(const Fp8PrepArgs& a) {
+  const int BH = a.B * a.H;
+  const int ntq = (a.N + kTile8 - 1) / kTile8;
+  const int64_t blocks = 3LL * BH * ntq;
+  hipLaunchKernelGGL((fp8_prepare_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kPrepThreads), 0,
+                     static_cast<hipStream_t>(a.stream), a.q, a.k, a.v, a.R, a.q8, a.k8, a.v8,
+                     a.sq, a.sk, a.sv, a.N, BH, ntq);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_one(const Fp8Args& a) {
+  const int BH = a.B * a.H;
+  const int nqb = (a.N + BR8 - 1) / BR8;
+  const int ntq = (a.N + kTile8 - 1) / kTile8;
+  const int64_t blocks = static_cast<int64_t>(nqb) * BH;
+  hipLaunchKernelGGL((attn_fp8_kernel<D, CAUSAL>), dim3(static_cast<unsigned>(blocks)), dim3(NT8), 0,
+                     static_cast<hipStream_t>(a.stream), a.q8, a.k8, a.v8, a.sq, a.sk, a.sv,
+                     static_cast<uint16_t*>(a.o), a.lse, a.N, BH, nqb, ntq, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8_prepare(const Fp8PrepArgs& a) {
+  return a.d == 64 ? prep_one<64>(a) : prep_one<128>(a);
+}
+
+hipError_t launch_fp8_fwd(const Fp8Args& a) {
+  if (a.d == 64) return a.causal ? fwd_one<64, true>(a) : fwd_one<64, false>(a);
+  return a.causal ? fwd_one<128, true>(a) : fwd_one<128, false>(a);
+}
+
 }  // namespace attn127

@@ -44,6 +44,9 @@
 //    head share one L2, heaviest causal blocks first.
 #include "common.h"
 #include "launch.h"
+#if defined(__HIP_DEVICE_COMPILE__)
+#include "device_util.h"
+#endif
 
 namespace attn127 {
 namespace {
@@ -81,39 +84,6 @@ constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100, kSgTrans = 0x
 
 // Device-only helpers (gfx950 builtins have no host-side meaning).
 #if defined(__HIP_DEVICE_COMPILE__)
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// generic pointer into a __shared__ array -> LDS address space (C-style cast:
-// the address-space change is not expressible with the C++ casts)
-__device__ __forceinline__ lds_void* as_lds(const char* p) { return (lds_void*)(const_cast<char*>(p)); }
-__device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<char*>(p)));
-}
-
-// Buffer descriptor for `bytes` bytes from `base`: reads past the end return 0.
-__device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{static_cast<int>(static_cast<uint32_t>(a)), static_cast<int>(static_cast<uint32_t>(a >> 32)),
-               static_cast<int>(bytes), 0x00020000};
-}
-
-// One 16-byte-per-lane HBM -> LDS copy: lane i's 16 bytes land at
-// lds_block + 16*i.  Issued as inline assembly so the compiler does not
-// serialise it against unrelated LDS reads; completion is tracked by the
-// explicit vmcnt waits of the tile loop.
-__device__ __forceinline__ void dma16(const i32x4& desc, const char* lds_block, int voffset) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(as_lds(lds_block))));
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(m), "v"(voffset), "s"(desc) : "memory", "m0");
-#pragma clang diagnostic pop
-}
-
 // Copy rows [kv0, kv0+BC) of one (b,h) slice of K or V into an LDS tile;
 // each wave copies BPW one-kilobyte blocks.
 template <int D, bool IS_V>
@@ -131,26 +101,6 @@ __device__ __forceinline__ void issue_copy(char* dst, const uint16_t* src, int k
     const int sw = IS_V ? vswz<D>(row) : kswz<D>(row);
     dma16(desc, dst + blk * 1024, row * C::ROWB + ((pos ^ sw) << 4));
   }
-}
-
-// Wait until at most n of this wave's vector-memory operations are in
-// flight (s_waitcnt vmcnt(n); the expcnt and lgkmcnt fields left at maximum).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
-}
-
-// v_permlane32_swap with both operands = x: lanes 0..31 get (own, partner),
-// lanes 32..63 get (partner, own), partner being the lane 32 away; combining
-// the pair gives the same two-lane reduction on every lane.
-__device__ __forceinline__ float halves_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D>

@@ -1,0 +1,209 @@
+"""fp8 (e4m3) path on the GPU against the float64 oracle.
+
+* attn_fp8_prepare: with an exactly representable rotation (a signed
+  permutation) the codes and tile scales must equal the oracle's bit for bit;
+  with a random orthogonal R the rotated values differ from the oracle's only
+  by float32 summation order, so codes may differ only next to a rounding
+  midpoint.
+* attn_fwd_fp8: compared with "oracle B" -- float64 attention on exactly the
+  dequantised inputs the kernel consumes (codes made by the oracle) -- under
+  |O - O_B| <= 6e-2 * max(1, |O_B|) (6e-2 ~ 2^-4, e4m3's relative spacing,
+  taken as relative once |O| > 1), and, for the fp8 workload without
+  outliers, with the unquantised oracle under max-abs <= 6e-2.  The literal
+  outlier workload against the unquantised oracle is printed, not gated:
+  input quantisation of the x40 channels alone moves O far beyond 6e-2.
+"""
+import numpy as np
+import pytest
+
+import exact_attention_127_amd as A
+import oracle
+from seeded_inputs import WORKLOADS, haar_orthogonal, make_inputs, random_inputs
+
+pytestmark = pytest.mark.gpu
+TOL8 = 6e-2
+
+
+def _dev(x, gpu, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(gpu) if dtype is None else t.to(gpu).to(dtype)
+
+
+def _gpu_prepare(inp, R, gpu):
+    import torch
+    outs = A.attn_fp8_prepare(*(_dev(inp[x].astype(np.float32), gpu) for x in "qkv"),
+                              _dev(np.asarray(R, np.float32), gpu))
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in outs]
+
+
+def _signed_permutation(d, rng):
+    P = np.zeros((d, d), np.float32)
+    P[np.arange(d), rng.permutation(d)] = rng.choice([-1.0, 1.0], d)
+    return P
+
+
+@pytest.mark.parametrize("N", [1, 128, 300])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prepare_exact_rotation_bit_exact(gpu, N, d):
+    rng = np.random.default_rng(N + d)
+    inp = random_inputs(2, 3, N, d, "f32", False, seed=N * 7 + d)
+    inp["q"][0, 1, :, 3] *= 40.0                     # an outlier channel
+    R = _signed_permutation(d, rng)
+    q8, k8, v8, sq, sk, sv = _gpu_prepare(inp, R, gpu)
+    (oq, osq), (ok, osk), (ov, osv) = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], R)
+    for got, want in ((q8, oq), (k8, ok), (v8, ov), (sq, osq), (sk, osk), (sv, osv)):
+        assert got.shape == want.shape
+        assert np.array_equal(got, want)
+
+
+def test_prepare_codec_edge_values(gpu):
+    """A V tile whose largest magnitude is 448 has scale 1, so its codes are
+    the e4m3 codes of the values themselves: midpoints (ties to even),
+    subnormals, the subnormal/normal boundary, saturation and signed zero."""
+    table = oracle.e4m3_table()
+    pos = table[:127]
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = np.concatenate([pos, -pos, mids, -mids, [0.0, -0.0, 447.9, 448.0, -448.0,
+                                                    2.0 ** -10, 2.0 ** -9 * 1.5, 15 / 1024]])
+    d, N = 64, 128
+    v = np.zeros((1, 1, N, d), np.float32)
+    flat = v.reshape(-1)
+    flat[:vals.size] = vals.astype(np.float32)
+    flat[vals.size] = 448.0
+    inp = {"q": v.copy(), "k": v.copy(), "v": v}
+    _, _, v8, _, _, sv = _gpu_prepare(inp, np.eye(d, dtype=np.float32), gpu)
+    (ov, osv) = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], np.eye(d))[2]
+    assert sv.item() == 1.0 == osv.item()
+    assert np.array_equal(v8, ov)
+
+
+def test_prepare_random_rotation(gpu):
+    w = WORKLOADS["fp8_outliers_8k"].with_(B=1, H=3, N=1000)
+    inp = make_inputs(w)
+    q8, k8, v8, sq, sk, sv = _gpu_prepare(inp, inp["R"], gpu)
+    (oq, osq), (ok, osk), (ov, osv) = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], inp["R"])
+    assert np.array_equal(v8, ov) and np.array_equal(sv, osv)
+    for got, want, gs, ws, x in ((q8, oq, sq, osq, inp["q"]), (k8, ok, sk, osk, inp["k"])):
+        assert np.allclose(gs, ws, rtol=2e-6, atol=0)
+        diff = got != want
+        # a code may differ only where the exact rotated value is within the
+        # float32 summation error bound (gamma_d * sum |x_i R_ic|, plus the
+        # scale's own rounding) of the midpoint between the two codes
+        x64 = x.astype(np.float64)
+        R64 = inp["R"].astype(np.float64)
+        y = np.matmul(x64, R64)
+        ysum = np.matmul(np.abs(x64), np.abs(R64))
+        dd = x.shape[-1]
+        gamma = dd * 2.0 ** -24 / (1 - dd * 2.0 ** -24)
+        s = np.repeat(ws.astype(np.float64), 128, axis=2)[:, :, :y.shape[2], None]
+        z = np.abs(y / s)
+        bound = (gamma * ysum + 2.0 ** -24 * np.abs(y)) / s + 4e-6 * z
+        lo = oracle.e4m3_decode(want & 0x7F)
+        hi = oracle.e4m3_decode(got & 0x7F)
+        mid = (lo + hi) / 2
+        assert np.all(np.abs(z[diff] - mid[diff]) <= bound[diff])
+        assert diff.mean() < 1e-3
+
+
+def _oracle_b(codes_scales, heads, rows, scale, causal):
+    (q8, sq), (k8, sk), (v8, sv) = codes_scales
+    qd, kd, vd = (oracle.fp8_dequantize(c, s) for c, s in ((q8, sq), (k8, sk), (v8, sv)))
+    os_, ls_ = [], []
+    for b, h in heads:
+        o, l = oracle.attention_rows(qd[b, h], kd[b, h], vd[b, h], scale, causal, rows)
+        os_.append(o)
+        ls_.append(l)
+    return np.stack(os_), np.stack(ls_)
+
+
+def _fwd_on_codes(cs, gpu, scale, causal):
+    import torch
+    (q8, sq), (k8, sk), (v8, sv) = cs
+    o, lse = A.attn_fwd_fp8(*(_dev(x, gpu) for x in (q8, k8, v8, sq, sk, sv)),
+                            scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("N", [1, 64, 129, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_vs_dequantised_oracle(gpu, N, d, causal):
+    inp = random_inputs(2, 2, N, d, "f32", causal, seed=31 * N + d + causal)
+    R = haar_orthogonal(np.random.default_rng(N).standard_normal((d, d))).astype(np.float32)
+    cs = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], R)
+    o, lse = _fwd_on_codes(cs, gpu, inp["scale"], causal)
+    rows = np.arange(N)
+    heads = [(b, h) for b in range(2) for h in range(2)]
+    ob, lb = _oracle_b(cs, heads, rows, inp["scale"], causal)
+    od = np.stack([o[b, h] for b, h in heads])
+    ld = np.stack([lse[b, h] for b, h in heads])
+    assert np.all(np.abs(od - ob) <= TOL8 * np.maximum(1.0, np.abs(ob)))
+    assert np.abs(od - ob).mean() < 5e-3
+    assert np.max(np.abs(ld - lb)) < 2e-2
+
+
+def _sample_heads(w, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(n)} | {(0, 0)})
+
+
+def test_fp8_workload_no_outliers_vs_unquantised(gpu):
+    """Gate G1: the fp8 workload's shapes, rotation and tile scales without the
+    outlier channels, full pipeline on the GPU, against the unquantised oracle."""
+    w = WORKLOADS["fp8_outliers_8k"].with_(outlier_frac=0.0, outlier_mult=1.0)
+    inp = make_inputs(w)
+    import torch
+    q8, k8, v8, sq, sk, sv = A.attn_fp8_prepare(*(_dev(inp[x], gpu) for x in "qkv"), _dev(inp["R"], gpu))
+    o, lse = A.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, scale=w.scale, causal=False)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    heads = _sample_heads(w, 4, 1)
+    rows = np.unique(np.concatenate([[0, w.N - 1], np.random.default_rng(2).integers(0, w.N, 48)]))
+    err = 0.0
+    for b, h in heads:
+        oa, _ = oracle.attention_rows(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.scale, False, rows)
+        err = max(err, float(np.abs(o[b, h][rows] - oa).max()))
+    print("fp8 without outliers vs unquantised oracle: max-abs", err)
+    assert err <= TOL8
+
+
+def test_fp8_workload_literal(gpu):
+    """Gate G2 on the literal fp8 workload (outliers x40 in Q, K and V).
+
+    The kernel runs on oracle-made codes of sampled heads at the full sequence
+    length (heads are independent, so a slice of heads is the same work per
+    head) and is compared with the dequantised-input oracle.  The full
+    GPU pipeline (prepare + forward, all heads) is then compared with the
+    unquantised oracle and printed beside the input-quantisation floor; with
+    x40 outliers a softmax this peaked can also pick a different key where
+    a rotated value sits on a rounding midpoint, so that comparison is
+    reported, not gated."""
+    w = WORKLOADS["fp8_outliers_8k"]
+    inp = make_inputs(w)
+    heads = _sample_heads(w, 3, 3)
+    rows = np.unique(np.concatenate([[0, w.N - 1], np.random.default_rng(4).integers(0, w.N, 64)]))
+    sl = {x: np.ascontiguousarray(np.stack([inp[x][b, h] for b, h in heads])[None]) for x in "qkv"}
+    cs = oracle.fp8_prepare(sl["q"], sl["k"], sl["v"], inp["R"])
+    o, _ = _fwd_on_codes(cs, gpu, w.scale, False)
+    ob, _ = _oracle_b(cs, [(0, i) for i in range(len(heads))], rows, w.scale, False)
+    od = o[0][:, rows]
+    rel = np.abs(od - ob) / np.maximum(1.0, np.abs(ob))
+    print(f"fp8 literal, kernel on oracle codes vs dequantised oracle: max rel {rel.max():.4f}, "
+          f"max-abs {np.abs(od - ob).max():.4f}")
+    assert rel.max() <= TOL8
+
+    import torch
+    q8, k8, v8, sq, sk, sv = A.attn_fp8_prepare(*(_dev(inp[x], gpu) for x in "qkv"), _dev(inp["R"], gpu))
+    of, _ = A.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, scale=w.scale, causal=False)
+    torch.cuda.synchronize()
+    of = of.float().cpu().numpy()
+    worst_a, floor_a = 0.0, 0.0
+    for i, (b, h) in enumerate(heads):
+        oa, _ = oracle.attention_rows(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.scale, False, rows)
+        worst_a = max(worst_a, float(np.abs(of[b, h][rows] - oa).max()))
+        floor_a = max(floor_a, float(np.abs(ob[i] - oa).max()))
+    print(f"fp8 literal, full GPU pipeline vs unquantised oracle: max-abs {worst_a:.3f} "
+          f"(input-quantisation floor {floor_a:.3f})")
