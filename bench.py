@@ -1,15 +1,16 @@
 """Benchmark: fused exact attention forward on one MI355X.
 
-One step = one attn_fwd call over the whole workload (every head, every
+One step = one forward call over the whole workload (every head, every
 query block, the full key loop), inputs resident in device memory.  The
 default workload is the long-sequence causal case B=1, H=16, N=16384,
 d=128, bf16.  Throughput counts 4*B*H*N^2*d FLOPs, halved for causal.
 
-Prints one JSON line.  ``roofline`` compares the measured rate with the
-published dense bf16 matrix-core peak; ``traffic`` is taken from a committed
-counter summary only while the kernel sources it was measured on are
-unchanged (else null).  ``cpu_baseline`` times the float64 CPU oracle on a
-bounded sample of the same workload on this host's cores.
+Prints one JSON line per workload.  ``roofline`` compares the kernel's rate
+(HIP events around the timed launches, on the launch stream) with the
+published dense matrix-core peak; ``traffic`` comes from a committed counter
+summary only while the kernel sources it was measured on are unchanged (else
+null).  ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of
+the same workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -21,26 +22,31 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # published MI355X dense peaks
-HBM_GBPS = 8000.0
-KERNEL_SOURCES = ["exact_attention_127_amd/csrc/attn_mfma_bf16.hip",
-                  "exact_attention_127_amd/csrc/common.h"]
+PEAK = {"bf16": 2500.0, "fp8": 5000.0}          # published MI355X dense TFLOP/s
+KERNEL_SOURCES = {
+    "bf16": ["exact_attention_127_amd/csrc/attn_mfma_bf16.hip",
+             "exact_attention_127_amd/csrc/device_util.h",
+             "exact_attention_127_amd/csrc/common.h"],
+    "fp8": ["exact_attention_127_amd/csrc/attn_fp8.hip",
+            "exact_attention_127_amd/csrc/device_util.h",
+            "exact_attention_127_amd/csrc/common.h"],
+}
 
 
-def kernel_hash() -> str:
+def kernel_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
+def traffic_from_profile(workload: str, kind: str):
     """Per-launch HBM bytes from a committed counter summary, if still valid."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_hash") != kernel_hash():
+    if rec.get("kernel_hash") != kernel_hash(kind):
         return None
     return rec.get("bytes_per_launch")
 
@@ -76,12 +82,97 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
                       f"{dt:.1f} s"}
 
 
+def timed(step, stream, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t_w = time.perf_counter()            # let the clocks settle: about a second of work
+    while time.perf_counter() - t_w < 1.0:
+        step()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
+def run_workload(name, args):
+    import torch
+    import exact_attention_127_amd as A
+    from seeded_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    stream = torch.cuda.current_stream()
+    extra = {}
+    if w.dtype == "bf16":
+        kind = "bf16"
+        q, k, v = (torch.from_numpy(inp[x]).to(dev).to(torch.bfloat16).contiguous() for x in "qkv")
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            A.attn_fwd(q, k, v, o=o, lse=lse, scale=w.scale, causal=w.causal, stream=stream)
+        peak = PEAK["bf16"]
+    elif w.dtype == "fp8":
+        kind = "fp8"
+        qf, kf, vf = (torch.from_numpy(inp[x]).to(dev).contiguous() for x in "qkv")
+        R = torch.from_numpy(inp["R"]).to(dev).contiguous()
+        prep = A.attn_fp8_prepare(qf, kf, vf, R)
+        q8, k8, v8, sq, sk, sv = prep
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        _, prep_ms = timed(lambda: A.attn_fp8_prepare(qf, kf, vf, R), stream, 3, 1)
+        prep_bytes = 3 * qf.numel() * 4 + 3 * qf.numel() + 3 * sq.numel() * 4 + R.numel() * 4
+        extra["prepare"] = {"ms": round(prep_ms, 4), "GB_per_s": round(prep_bytes / prep_ms / 1e6, 1)}
+
+        def step():
+            A.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, o=o, lse=lse, scale=w.scale, causal=w.causal,
+                           stream=stream)
+        # scores on fp8, P V on bf16: time-weighted peak of the two halves
+        peak = 1.0 / (0.5 / PEAK["fp8"] + 0.5 / PEAK["bf16"])
+    else:
+        raise SystemExit(f"bench.py times the bf16 and fp8 workloads, not {name}")
+
+    ms_per_step, kernel_ms = timed(step, stream, args.steps, args.warmup)
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    line = {
+        "metric": "attn fwd TFLOP/s + % of bf16 MFMA peak, B=1 H=16 N=16384 d=128 causal"
+        if name == "long_causal_16k" else f"attn fwd TFLOP/s, {name}",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "seed": w.seed, "flops_per_step": w.flops,
+                   "pct_of_peak": round(100 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_from_profile(w.name, kind),
+                     "kernel_ms": round(kernel_ms, 4), "kernel_hash": kernel_hash(kind)},
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long_causal_16k")
+    ap.add_argument("--workload", default="long_causal_16k",
+                    help="workload name, or 'all' for one line per bf16/fp8 workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB per step (counter calibration)")
@@ -93,9 +184,6 @@ def main() -> int:
         return 2
 
     import torch
-    import exact_attention_127_amd as A
-    from seeded_inputs import WORKLOADS, make_inputs
-
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
         dst = torch.empty_like(src)
@@ -105,60 +193,10 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2,
                           "launches": args.warmup + args.steps}))
         return 0
-
-    w = WORKLOADS[args.workload]
-    if w.dtype != "bf16":
-        print("bench.py times the bf16 workloads", file=sys.stderr)
-        return 2
-    dev = torch.device("cuda:0")
-    inp = make_inputs(w)
-    q, k, v = (torch.from_numpy(inp[x]).to(dev).to(torch.bfloat16).contiguous() for x in "qkv")
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        A.attn_fwd(q, k, v, o=o, lse=lse, scale=w.scale, causal=w.causal, stream=stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # keep warming until the clocks have settled (about one second of work)
-    t_w = time.perf_counter()
-    while time.perf_counter() - t_w < 1.0:
-        step()
-        torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps          # one launch per step
-    ms_per_step = wall * 1e3 / args.steps
-    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS["bf16"]
-    line = {
-        "metric": "attn fwd TFLOP/s + % of bf16 MFMA peak, B=1 H=16 N=16384 d=128 causal"
-        if args.workload == "long_causal_16k" else f"attn fwd TFLOP/s, {args.workload}",
-        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "seed": w.seed, "flops_per_step": w.flops,
-                   "pct_of_bf16_peak": round(100 * tflops / peak, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_from_profile(w.name),
-                     "kernel_ms": round(kernel_ms, 4), "kernel_hash": kernel_hash()},
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp)
-    print(json.dumps(line), flush=True)
+    names = ([args.workload] if args.workload != "all" else
+             ["long_causal_16k", "vit_b16_batch64", "llm_layer_4k", "fp8_outliers_8k"])
+    for n in names:
+        run_workload(n, args)
     return 0
 
 
