@@ -51,16 +51,17 @@
 namespace attn127 {
 namespace {
 
-constexpr int NW = 4;            // waves per workgroup (one per SIMD)
 constexpr int BRW = 32;          // query rows per wave
-constexpr int BR = NW * BRW;     // query rows per workgroup
 constexpr int BC = 64;           // keys per tile
-constexpr int NT = NW * 64;      // threads per workgroup
 constexpr float kTau = 8.0f;     // allowed growth of p above 1, as a power of two
 constexpr int kXcds = 8;
 
-template <int D>
+// NW waves per workgroup: 8 (two per SIMD, sharing each K/V tile) or 4
+// (one per SIMD, two workgroups per CU).
+template <int D, int NW>
 struct Cfg {
+  static constexpr int NT = NW * 64;           // threads per workgroup
+  static constexpr int BR = NW * BRW;          // query rows per workgroup
   static constexpr int ROWB = D * 2;           // bytes per K/V row
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int RPB = 1024 / ROWB;      // rows per 1 KB copy block
@@ -68,6 +69,7 @@ struct Cfg {
   static constexpr int BLK = TILEB / 1024;     // 1 KB blocks per tile
   static constexpr int BPW = BLK / NW;         // blocks of one tile copied per wave
   static_assert(BPW * NW == BLK, "tile must split evenly over the waves");
+  static_assert(2 * BPW < 16, "vmcnt field");
 };
 
 // Chunk swizzles (XOR on the 16-byte chunk index within a row).  K: the 16
@@ -86,10 +88,10 @@ constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100, kSgTrans = 0x
 #if defined(__HIP_DEVICE_COMPILE__)
 // Copy rows [kv0, kv0+BC) of one (b,h) slice of K or V into an LDS tile;
 // each wave copies BPW one-kilobyte blocks.
-template <int D, bool IS_V>
+template <int D, int NW, bool IS_V>
 __device__ __forceinline__ void issue_copy(char* dst, const uint16_t* src, int kv0, int N,
                                            int wave, int lane) {
-  using C = Cfg<D>;
+  using C = Cfg<D, NW>;
   const int rows = min(BC, N - kv0);
   const i32x4 desc = buffer_desc(src + static_cast<int64_t>(kv0) * D,
                                  static_cast<uint32_t>(rows) * C::ROWB);
@@ -121,7 +123,7 @@ struct LaneAddr {
   int kofs[D / 16];
   int vbase[D / 32];
   __device__ __forceinline__ LaneAddr(int j, int h, int lane) {
-    using C = Cfg<D>;
+    using C = Cfg<D, 4>;        // only the row size is used
     const int ksw = kswz<D>(j);   // rows j and 32+j share the swizzle
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) kofs[ks] = j * C::ROWB + (((2 * ks + h) ^ ksw) << 4);
@@ -145,21 +147,21 @@ __device__ __forceinline__ void scores(f32x16 (&sacc)[BC / 32], const WaveState<
     sacc[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * Cfg<D>::ROWB + la.kofs[ks]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * (2 * D) + la.kofs[ks]);
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qr[ks], sacc[kb], 0, 0, 0);
     }
   }
 }
 
 // Keys past the diagonal (causal) or past the sequence end -> -inf.
-template <bool CAUSAL>
-__device__ __forceinline__ void apply_mask(f32x16 (&sacc)[BC / 32], int kv0, int N, int qrow, int h) {
+__device__ __forceinline__ void apply_mask(f32x16 (&sacc)[BC / 32], int kv0, int N, int qrow, int h,
+                                           bool causal) {
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      const bool masked = (key >= N) || (CAUSAL && key > qrow);
+      const bool masked = (key >= N) || (causal && key > qrow);
       sacc[kb][r] = masked ? -INFINITY : sacc[kb][r];
     }
 }
@@ -221,8 +223,8 @@ __device__ __forceinline__ void pv_tile(WaveState<D>& w, const bf16x8 (&pb)[BC /
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int c16 = 0; c16 < BC / 16; ++c16) {
-      const v4i16 lo = ds_read_tr16(vst + la.vbase[db] + (c16 * 16) * Cfg<D>::ROWB);
-      const v4i16 hi = ds_read_tr16(vst + la.vbase[db] + (c16 * 16 + 8) * Cfg<D>::ROWB);
+      const v4i16 lo = ds_read_tr16(vst + la.vbase[db] + (c16 * 16) * (2 * D));
+      const v4i16 hi = ds_read_tr16(vst + la.vbase[db] + (c16 * 16 + 8) * (2 * D));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c16], w.oacc[db], 0, 0, 0);
     }
@@ -252,13 +254,13 @@ __device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32
 
 // Phase B: P V of the current tile on the matrix cores, interleaved with the
 // (masked) row maximum of the next tile on the vector ALUs.
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool MASK>
 __device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32],
                                          const bf16x8 (&pb)[BC / 16], const LaneAddr<D>& la,
-                                         const char* vst, int kv0n, int N, int qrow, int h) {
+                                         const char* vst, int kv0n, int N, int qrow, int h, bool causal) {
   __builtin_amdgcn_sched_barrier(0);
   pv_tile<D>(w, pb, la, vst);
-  if (MASK) apply_mask<CAUSAL>(snext, kv0n, N, qrow, h);
+  if (MASK) apply_mask(snext, kv0n, N, qrow, h, causal);
   const float mx = tile_max(snext);
   constexpr int nm = (D / 32) * (BC / 16);
   __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
@@ -273,13 +275,18 @@ __device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 3
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(NT, 2)
+// The causal flag is a run-time argument: the causal and non-causal launches
+// share one compiled loop (a compile-time flag let the compiler allocate the
+// non-causal loop into register spills).
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                      float* __restrict__ lse, int N, int BH, int nqb, float c) {
+                      float* __restrict__ lse, int N, int BH, int nqb, float c, int causal_arg) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = Cfg<D>;
+  using C = Cfg<D, NW>;
+  constexpr int BR = C::BR;
+  const bool causal = causal_arg != 0;
   // two-slot rings for K and V tiles
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILEB];
   char* const kring = smem;
@@ -296,9 +303,9 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   int bh, qb;
   if (BH % kXcds == 0) {
     const int x = id % kXcds, s = id / kXcds, hx = BH / kXcds;
-    if (CAUSAL) { qb = nqb - 1 - s / hx; bh = x + kXcds * (s % hx); }
+    if (causal) { qb = nqb - 1 - s / hx; bh = x + kXcds * (s % hx); }
     else        { bh = x + kXcds * (s / nqb); qb = s % nqb; }
-  } else if (CAUSAL) {
+  } else if (causal) {
     qb = nqb - 1 - id / BH; bh = id % BH;
   } else {
     bh = id / nqb; qb = id % nqb;
@@ -317,16 +324,16 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   w.lsum = 0.f;
   const LaneAddr<D> la(j, h, lane);
 
-  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const int kend = causal ? min(N, q0 + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
   // last tile this wave needs (-1: the wave's rows are all past the end)
   int last = -1;
-  if (q0w < N) last = CAUSAL ? min(ntiles - 1, (q0w + BRW - 1) / BC) : ntiles - 1;
+  if (q0w < N) last = causal ? min(ntiles - 1, (q0w + BRW - 1) / BC) : ntiles - 1;
 
   // ---- prologue: K0, V0, K1 and Q in flight; scores of tile 0 ----
-  issue_copy<D, false>(kring, kbase, 0, N, wave, lane);
-  issue_copy<D, true>(vring, vbase, 0, N, wave, lane);
-  if (ntiles > 1) issue_copy<D, false>(kring + C::TILEB, kbase, BC, N, wave, lane);
+  issue_copy<D, NW, false>(kring, kbase, 0, N, wave, lane);
+  issue_copy<D, NW, true>(vring, vbase, 0, N, wave, lane);
+  if (ntiles > 1) issue_copy<D, NW, false>(kring + C::TILEB, kbase, BC, N, wave, lane);
   {
     const int rows = max(0, min(BRW, N - q0w));
     const auto rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -345,7 +352,7 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   bf16x8 pb[BC / 16];
   if (last >= 0) {
     scores<D>(sa, w, la, kring, h);
-    if ((CAUSAL && BC - 1 > q0w) || BC > N) apply_mask<CAUSAL>(sa, 0, N, qrow, h);
+    if ((causal && BC - 1 > q0w) || BC > N) apply_mask(sa, 0, N, qrow, h, causal);
     update_reference<D>(w, halves_max(tile_max(sa)) * c);
   }
   __syncthreads();   // every wave is done with K0 before its slot is refilled
@@ -358,15 +365,15 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   auto iteration = [&](int t, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32]) {
     const char* kst_next = kring + ((t + 1) & 1) * C::TILEB;
     const char* vst = vring + (t & 1) * C::TILEB;
-    if (t + 1 < ntiles) issue_copy<D, true>(vring + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave, lane);
-    if (t + 2 < ntiles) issue_copy<D, false>(kring + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
+    if (t + 1 < ntiles) issue_copy<D, NW, true>(vring + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave, lane);
+    if (t + 2 < ntiles) issue_copy<D, NW, false>(kring + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
     if (t < last) {
       const int kv0n = (t + 1) * BC;
       phase_a<D>(w, snext, pb, scur, la, kst_next, h, c);
-      const bool mask_next = (CAUSAL && kv0n + BC - 1 > q0w) || (kv0n + BC > N);
+      const bool mask_next = (causal && kv0n + BC - 1 > q0w) || (kv0n + BC > N);
       float mx;
-      if (mask_next) mx = phase_b<D, CAUSAL, true>(w, snext, pb, la, vst, kv0n, N, qrow, h);
-      else           mx = phase_b<D, CAUSAL, false>(w, snext, pb, la, vst, kv0n, N, qrow, h);
+      if (mask_next) mx = phase_b<D, true>(w, snext, pb, la, vst, kv0n, N, qrow, h, causal);
+      else           mx = phase_b<D, false>(w, snext, pb, la, vst, kv0n, N, qrow, h, causal);
       update_reference<D>(w, halves_max(mx) * c);
     } else if (t == last) {
       softmax_tile<D>(w, pb, scur, c);
@@ -401,24 +408,27 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool CAUSAL>
+template <int D, int NW>
 hipError_t launch_one(const LaunchArgs& a) {
+  using C = Cfg<D, NW>;
   const int BH = a.B * a.H;
-  const int nqb = (a.N + BR - 1) / BR;
+  const int nqb = (a.N + C::BR - 1) / C::BR;
   const int64_t blocks = static_cast<int64_t>(nqb) * BH;
-  hipLaunchKernelGGL((attn_mfma_bf16_kernel<D, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(NT), 0, static_cast<hipStream_t>(a.stream),
+  hipLaunchKernelGGL((attn_mfma_bf16_kernel<D, NW>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(C::NT), 0, static_cast<hipStream_t>(a.stream),
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                     a.N, BH, nqb, a.scale * kLog2e);
+                     a.N, BH, nqb, a.scale * kLog2e, a.causal);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// d = 128: eight waves (two per SIMD, one K/V tile copy shared by 256 query
+// rows) measured faster than four.  d = 64 (short sequences): four waves,
+// 128 rows per workgroup and two workgroups per CU.
 hipError_t launch_mfma_bf16(const LaunchArgs& a) {
-  if (a.d == 64) return a.causal ? launch_one<64, true>(a) : launch_one<64, false>(a);
-  return a.causal ? launch_one<128, true>(a) : launch_one<128, false>(a);
+  return a.d == 64 ? launch_one<64, 4>(a) : launch_one<128, 8>(a);
 }
 
 }  // namespace attn127
