@@ -39,7 +39,9 @@ constexpr float kE4m3Max = 448.0f;
 // ---------------------------------------------------------------------------
 // prepare
 // ---------------------------------------------------------------------------
-constexpr int kPrepThreads = 256;
+// 4*d threads: each computes 4 tokens x 8 channels of the rotated tile
+template <int D>
+constexpr int prep_threads() { return 4 * D; }
 
 #if defined(__HIP_DEVICE_COMPILE__)
 // Nearest e4m3 (E4M3FN) code of x: ties to even, |x| >= 448 saturates to
@@ -64,16 +66,17 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
 #endif
 
 template <int D>
-__global__ void __launch_bounds__(kPrepThreads)
+__global__ void __launch_bounds__(prep_threads<D>())
 fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
                    const float* __restrict__ v, const float* __restrict__ R,
                    uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, uint8_t* __restrict__ v8,
                    float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv,
                    int N, int BH, int ntq) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int TP = kTile8 + 1;                 // padded token stride of the transposed tile
-  __shared__ float xt[D * TP];                   // x^T: xt[c*TP + token]
-  __shared__ float rs[D * D];                    // R row-major
+  constexpr int TP = kTile8 + 4;                 // token stride of the transposed tile (16-byte rows)
+  __shared__ __attribute__((aligned(16))) float xt[D * TP];   // x^T: xt[c*TP + token]
+  __shared__ __attribute__((aligned(16))) float rs[D * D];    // R row-major
+  constexpr int kPrepThreads = prep_threads<D>();
   __shared__ float red[kPrepThreads / 64];
 
   const int tid = threadIdx.x;
@@ -94,12 +97,14 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
     xt[col * TP + r] = (r < rows) ? src[off + static_cast<int64_t>(r) * D + col] : 0.f;
   }
   if (rotate)
-    for (int e = tid; e < D * D; e += kPrepThreads) rs[e] = R[e];
+    for (int e = tid * 4; e < D * D; e += kPrepThreads * 4)
+      *reinterpret_cast<f32x4*>(rs + e) = *reinterpret_cast<const f32x4*>(R + e);
   __syncthreads();
 
   // each thread: TT tokens x 8 channels
   constexpr int CG = D / 8;                      // channel groups
-  constexpr int TT = kTile8 * CG / kPrepThreads; // tokens per thread (8 for D=128, 4 for D=64)
+  constexpr int TT = kTile8 * CG / kPrepThreads; // tokens per thread (4)
+  static_assert(TT % 4 == 0, "tokens per thread come in 16-byte groups");
   const int cc = (tid % CG) * 8;
   const int tt = (tid / CG) * TT;
   float y[TT][8];
@@ -111,9 +116,14 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
     for (int i = 0; i < D; ++i) {
       float a[TT], b[8];
 #pragma unroll
-      for (int r = 0; r < TT; ++r) a[r] = xt[i * TP + tt + r];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) b[c] = rs[i * D + cc + c];
+      for (int r = 0; r < TT; r += 4) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(xt + i * TP + tt + r);
+        a[r] = x4[0]; a[r + 1] = x4[1]; a[r + 2] = x4[2]; a[r + 3] = x4[3];
+      }
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(rs + i * D + cc);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(rs + i * D + cc + 4);
+      b[0] = b0[0]; b[1] = b0[1]; b[2] = b0[2]; b[3] = b0[3];
+      b[4] = b1[0]; b[5] = b1[1]; b[6] = b1[2]; b[7] = b1[3];
 #pragma unroll
       for (int r = 0; r < TT; ++r)
 #pragma unroll
@@ -431,7 +441,7 @@ hipError_t prep_one(const Fp8PrepArgs& a) {
   const int BH = a.B * a.H;
   const int ntq = (a.N + kTile8 - 1) / kTile8;
   const int64_t blocks = 3LL * BH * ntq;
-  hipLaunchKernelGGL((fp8_prepare_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kPrepThreads), 0,
+  hipLaunchKernelGGL((fp8_prepare_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(prep_threads<D>()), 0,
                      static_cast<hipStream_t>(a.stream), a.q, a.k, a.v, a.R, a.q8, a.k8, a.v8,
                      a.sq, a.sk, a.sv, a.N, BH, ntq);
   return hipGetLastError();
