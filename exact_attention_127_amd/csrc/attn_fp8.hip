@@ -166,6 +166,7 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
 // forward
 // ---------------------------------------------------------------------------
 constexpr int NW8 = 4;               // waves per workgroup
+constexpr int kXcds8 = 8;            // XCDs the dispatcher round-robins over
 constexpr int BR8 = NW8 * 32;        // query rows per workgroup (one quantisation tile)
 constexpr int BC8 = 64;              // keys per tile (half a quantisation tile)
 constexpr int NT8 = NW8 * 64;
@@ -266,10 +267,20 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   const int j = lane & 31;
   const int h = lane >> 5;
 
+  // Work item: workgroups are dispatched round-robin over the 8 XCDs, so
+  // item id lands on XCD id % 8; giving each XCD whole heads keeps a head's
+  // K/V tiles in one L2.  Causal: heaviest query blocks first.
   const int id = static_cast<int>(blockIdx.x);
   int bh, qbk;
-  if (CAUSAL) { qbk = nqb - 1 - id / BH; bh = id % BH; }
-  else        { bh = id / nqb; qbk = id % nqb; }
+  if (BH % kXcds8 == 0) {
+    const int x = id % kXcds8, s = id / kXcds8, hx = BH / kXcds8;
+    if (CAUSAL) { qbk = nqb - 1 - s / hx; bh = x + kXcds8 * (s % hx); }
+    else        { bh = x + kXcds8 * (s / nqb); qbk = s % nqb; }
+  } else if (CAUSAL) {
+    qbk = nqb - 1 - id / BH; bh = id % BH;
+  } else {
+    bh = id / nqb; qbk = id % nqb;
+  }
   const int q0 = qbk * BR8;
   const int q0w = q0 + wave * 32;
   const int qrow = q0w + j;
