@@ -23,6 +23,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK = {"bf16": 2500.0, "fp8": 5000.0}          # published MI355X dense TFLOP/s
+HBM_PEAK_GBS = 8000.0                            # published MI355X HBM3E bandwidth
 KERNEL_SOURCES = {
     "bf16": ["exact_attention_127_amd/csrc/attn_mfma_bf16.hip",
              "exact_attention_127_amd/csrc/device_util.h",
@@ -104,6 +105,28 @@ def timed(step, stream, steps, warmup):
     return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
+def algorithmic_bytes(w, kind: str) -> int:
+    """Q, K, V read once (2 B per element in bf16, 1 B in fp8), O (bf16) and
+    LSE (float32) written once."""
+    in_bytes = 2 if kind == "bf16" else 1
+    return w.B * w.H * w.N * (3 * in_bytes * w.d + 2 * w.d + 4)
+
+
+def roofline(w, kind: str, kernel_ms: float, peak_tflops: float):
+    """The bound that applies to one launch of workload ``w``: HBM when moving
+    its algorithmic bytes at peak bandwidth takes longer than its FLOPs at
+    peak matrix-core rate, else the matrix cores."""
+    alg_bytes = algorithmic_bytes(w, kind)
+    if alg_bytes / (HBM_PEAK_GBS * 1e9) > w.flops / (peak_tflops * 1e12):
+        roof = {"bound": "hbm", "achieved": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(w.flops / (kernel_ms * 1e-3) / 1e12, 2),
+                "peak": round(peak_tflops, 1), "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    return roof, alg_bytes
+
+
 def run_workload(name, args):
     import torch
     import exact_attention_127_amd as A
@@ -145,7 +168,7 @@ def run_workload(name, args):
 
     ms_per_step, kernel_ms = timed(step, stream, args.steps, args.warmup)
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    roof, alg_bytes = roofline(w, kind, kernel_ms, peak)
     line = {
         "metric": "attn fwd TFLOP/s + % of bf16 MFMA peak, B=1 H=16 N=16384 d=128 causal"
         if name == "long_causal_16k" else f"attn fwd TFLOP/s, {name}",
@@ -155,9 +178,8 @@ def run_workload(name, args):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "seed": w.seed, "flops_per_step": w.flops,
                    "pct_of_peak": round(100 * tflops / peak, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_from_profile(w.name, kind),
+        "roofline": {**roof, "traffic": traffic_from_profile(w.name, kind),
+                     "algorithmic_bytes": alg_bytes,
                      "kernel_ms": round(kernel_ms, 4), "kernel_hash": kernel_hash(kind)},
     }
     line.update(extra)
