@@ -17,21 +17,29 @@ Sources followed (page title, section):
     section 1, FP8 bullet (block quantisation with an independent scale per
     small tile; incoherent processing: Q and K multiplied by a random
     orthogonal matrix before quantisation).
+  * The backward pass of the first page, section 3 (only small statistics
+    are kept; tiles are recomputed): ``backward`` holds the gradients of the
+    forward definition, written out by the chain rule.
 
 Pins (tests/test_oracle*.py): high-precision brute force on tiny inputs,
 hand-worked closed forms (tests/golden/), invariants (rows of P sum to one,
 Q = 0 gives the mean of the visible V rows, causal row 0 equals V[0], a
 dominant score selects one V row, invariance under a common orthogonal
 rotation of Q and K, linearity in V), and the e4m3 / bf16 codecs against the
-OCP 8-bit floating-point definition and torch's casts.  Every function here is
-pinned; none is "parity unpinned".
+OCP 8-bit floating-point definition and torch's casts; the gradients against
+central finite differences of the forward oracle and against invariants (the
+dK rows sum to zero, the dV rows sum to the dO rows, identical keys give
+dQ = 0).  Every function here is pinned; none is "parity unpinned".
 """
 from .exact import attention, attention_rows, attention_probs, lse_rows
 from .formats import (bf16_round, bf16_half_ulp, e4m3_decode, e4m3_encode,
                       E4M3_MAX, e4m3_table)
 from .fp8 import fp8_prepare, fp8_dequantize, QUANT_TILE
+from .backward import (attention_backward, attention_backward_head, row_delta,
+                       dq_rows, dkdv_cols)
 
 __all__ = ["attention", "attention_rows", "attention_probs", "lse_rows",
            "bf16_round", "bf16_half_ulp", "e4m3_decode", "e4m3_encode",
            "E4M3_MAX", "e4m3_table", "fp8_prepare", "fp8_dequantize",
-           "QUANT_TILE"]
+           "QUANT_TILE", "attention_backward", "attention_backward_head",
+           "row_delta", "dq_rows", "dkdv_cols"]
