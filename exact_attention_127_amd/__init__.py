@@ -11,6 +11,7 @@ The functions keep the C names:
     attn_fwd_simple(...)                       same contract, plain kernel
     attn_fp8_prepare(q, k, v, R)               -> (q8, k8, v8, sq, sk, sv)
     attn_fwd_fp8(q8, k8, v8, sq, sk, sv, ...)  -> (o, lse)
+    attn_bwd(q, k, v, o, dout, lse, ...)       -> (dq, dk, dv)
     attn_strerror(status)
 """
 from __future__ import annotations
@@ -21,14 +22,14 @@ import os
 
 import torch  # loads the HIP runtime that the library then shares
 
-__all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
+__all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd",
            "attn_strerror", "AttnError", "AttnLibraryMissing", "lib", "LIB_PATH",
            "EXPORTED_SYMBOLS", "ATTN_F32", "ATTN_BF16", "FP8_TILE"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn127.so")
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
-                    "attn_strerror")
+                    "attn_bwd", "attn_strerror")
 ATTN_F32, ATTN_BF16 = 0, 1
 FP8_TILE = 128
 _STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fp8_prepare.restype = _I
         L.attn_fwd_fp8.argtypes = [_P] * 8 + [_I, _I, _I, _I, _F, _I, _P]
         L.attn_fwd_fp8.restype = _I
+        L.attn_bwd.argtypes = [_P] * 10 + [_I, _I, _I, _I, _F, _I, _I, _P]
+        L.attn_bwd.restype = _I
         L.attn_strerror.argtypes = [_I]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -170,3 +173,37 @@ def attn_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, scale=None, causal=Fa
                             _stream(stream))
     _check(st, "attn_fwd_fp8")
     return o, lse
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, scale=None,
+             causal=False, stream=None):
+    """dQ, dK, dV of attn_fwd (bf16), from the forward's O and LSE and the
+    output gradient dout.  ``delta`` is float32 [B, H, N] scratch (allocated
+    here when not given)."""
+    if q.dim() != 4:
+        raise ValueError("q, k, v, o, dout must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for t in (q, k, v, o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, o, dout must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("q, k, v, o, dout must be contiguous")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("attn_bwd takes bfloat16 tensors")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous bfloat16 like q")
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+                        _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                        int(bool(causal)), ATTN_BF16, _stream(stream))
+    _check(st, "attn_bwd")
+    return dq, dk, dv

@@ -100,6 +100,26 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const 
   return status_of(attn127::launch_fp8_fwd(a));
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int N,
+             int d, float scale, int causal, int dtype, void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (check_scale(scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  const void* ps[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  if (!lse || !delta) return ATTN_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  if (st == 1) return ATTN_OK;
+  attn127::BwdArgs a{q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale,
+                     causal ? 1 : 0, stream};
+  return status_of(attn127::launch_bwd(a));
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -1,0 +1,468 @@
+// Backward pass of exact attention on bf16 matrix cores (gfx950).
+//
+// The page "Self-Attention, CUDA kernels and FlashAttention", section 3:
+// the backward pass keeps only the small per-row statistics of the forward
+// pass (here the natural-log LSE) and recomputes the attention tiles on chip.
+// With c = scale*log2(e), per head:
+//   P   = exp2(c*Q K^T - log2(e)*LSE)        recomputed tile by tile (masked)
+//   dV  = P^T dO
+//   dP  = dO V^T
+//   D_i = sum_c dO_ic O_ic                   (equals sum_j P_ij dP_ij)
+//   dS  = P * (dP - D)
+//   dQ  = scale * dS K,   dK = scale * dS^T Q
+// Nothing N x N reaches memory.  Three launches, no atomics:
+//  * bwd_delta_kernel: D for every row (HBM-bound).
+//  * bwd_dkdv_kernel: one workgroup per (b*h, block of keys); K and V of the
+//    block sit in LDS, Q / dO tiles stream through a two-slot ring.  Each
+//    wave owns 32 keys, so S = Q K^T and dP = dO V^T are computed with the
+//    key in the accumulator column: every lane holds 16 queries of one key,
+//    which is the B-operand layout that dV^T += dO^T P and dK^T += Q^T dS
+//    need (dO^T, Q^T come from transposing LDS reads).
+//  * bwd_dq_kernel: one workgroup per (b*h, block of queries), laid out like
+//    the forward kernel: S^T = K Q^T and dP^T = V dO^T put the query in the
+//    column, so LSE and D are one register per lane, and dQ^T += K^T dS^T
+//    reads K^T through transposing LDS reads.
+// K, V, Q and dO tiles are each read both row-wise (16-byte reads) and
+// transposed (ds_read_b64_tr_b16); one XOR swizzle of the 16-byte chunks
+// keeps both patterns free of LDS bank conflicts.
+#include "common.h"
+#include "launch.h"
+#if defined(__HIP_DEVICE_COMPILE__)
+#include "device_util.h"
+#endif
+
+namespace attn127 {
+namespace {
+
+constexpr int BT = 64;        // rows per streamed tile (keys in dQ, queries in dK/dV)
+constexpr int kXcdsB = 8;     // XCDs the dispatcher round-robins over
+
+template <int D>
+struct BTile {
+  static constexpr int ROWB = 2 * D;          // bytes per bf16 row
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int RPB = 1024 / ROWB;     // rows per 1 KB copy block
+  static constexpr int TILEB = BT * ROWB;     // bytes of one tile
+  static constexpr int BLK = TILEB / 1024;    // 1 KB blocks per tile
+};
+
+// Chunk swizzle of row `row`.  d=128 (16 chunks, 256-byte rows): the
+// row-wise reads of 16 consecutive rows need 16 distinct chunk positions
+// (the two 2-bit fields of the row's low nibble, swapped, are a bijection),
+// and the 4 rows x 2 chunks of one transposing read need 8 (the row's low
+// two bits move the chunk's high bits).  d=64 (8 chunks, 128-byte rows, two
+// rows per bank window): the same two requirements per row parity.
+template <int D>
+__host__ __device__ constexpr int bswz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 1) | (((row >> 2) & 1) << 2) | ((row >> 3) & 1));
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// Buffer descriptor forced into scalar registers (the copy instructions take
+// it as a scalar operand; every field is the same on all lanes).
+__device__ __forceinline__ i32x4 uniform_desc(const void* base, uint32_t bytes) {
+  const i32x4 d = buffer_desc(base, bytes);
+  return i32x4{__builtin_amdgcn_readfirstlane(d[0]), __builtin_amdgcn_readfirstlane(d[1]),
+               __builtin_amdgcn_readfirstlane(d[2]), __builtin_amdgcn_readfirstlane(d[3])};
+}
+
+// One 4-byte-per-lane HBM -> LDS copy: lane i's word lands at lds + 4*i.
+__device__ __forceinline__ void dma4(const i32x4& desc, const char* lds_block, int voffset) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(as_lds(lds_block))));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m), "v"(voffset), "s"(desc) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Rows [r0, r0+BT) of a [N][D] bf16 slice -> one LDS tile (rows past N read
+// as zero); the workgroup's NW waves share the tile's 1 KB blocks.
+template <int D, int NW>
+__device__ __forceinline__ void copy_tile(char* dst, const uint16_t* src, int r0, int N, int wave,
+                                          int lane) {
+  using T = BTile<D>;
+  static_assert(T::BLK % NW == 0, "tile must split evenly over the waves");
+  constexpr int BPW = T::BLK / NW;
+  const int rows = min(BT, N - r0);
+  const i32x4 desc = uniform_desc(src + static_cast<int64_t>(r0) * D,
+                                  static_cast<uint32_t>(max(rows, 0)) * T::ROWB);
+#pragma unroll
+  for (int b = 0; b < BPW; ++b) {
+    const int blk = wave * BPW + b;
+    const int row = blk * T::RPB + lane / T::CPR;
+    const int pos = lane % T::CPR;
+    dma16(desc, dst + blk * 1024, row * T::ROWB + ((pos ^ bswz<D>(row)) << 4));
+  }
+}
+
+// Lane-constant LDS offsets.  Row reads (operand rows j and j+32 of a tile,
+// channels 16ks+8h..+7): rofs[ks].  Transposing reads of channel block db:
+// rows key0 + 8i (+16 per 16-row group), tofs[db][i]; the swizzle of those
+// rows depends only on i.
+template <int D>
+struct BLane {
+  int rofs[D / 16];
+  int tofs[D / 32][2];
+  __device__ __forceinline__ BLane(int j, int h, int lane) {
+    using T = BTile<D>;
+    const int sj = bswz<D>(j);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) rofs[ks] = j * T::ROWB + (((2 * ks + h) ^ sj) << 4);
+    const int r16 = lane & 15, b16 = (lane >> 4) & 1;
+    const int key0 = 4 * h + (r16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int chunk = db * 4 + 2 * b16 + ((r16 & 3) >> 1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = key0 + 8 * i;
+        tofs[db][i] = row * T::ROWB + ((chunk ^ bswz<D>(row)) << 4) + ((r16 & 1) << 3);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds_row(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Transposed operand: channels 32db + lane%32, 16 rows of group g16 (rows
+// 16 g16 .. +15 of the tile) in the order of a 32x32 accumulator's rows.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_trans(const char* tile, const BLane<D>& la, int db, int g16) {
+  const int off = g16 * 16 * BTile<D>::ROWB;
+  const v4i16 lo = ds_read_tr16(tile + la.tofs[db][0] + off);
+  const v4i16 hi = ds_read_tr16(tile + la.tofs[db][1] + off);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Store a 32x32 accumulator block whose column is this lane's row `row` of
+// a [N][D] output and whose rows are channels 32db + 8g + 4h + (0..3),
+// multiplied by `mul`, as bf16.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc)[D / 32], int h,
+                                           float mul) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 wv;
+      wv[0] = pack_bf16x2(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
+      wv[1] = pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+      *reinterpret_cast<u32x2*>(out_row + db * 32 + 8 * g + 4 * h) = wv;
+    }
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
+// ---- D_i = sum_c dO_ic O_ic, float32, one row per D/8 lanes ----
+template <int D>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(const uint16_t* __restrict__ o,
+                                                        const uint16_t* __restrict__ dout,
+                                                        float* __restrict__ delta, int64_t rows) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int LPR = D / 8;          // lanes per row, 8 elements each
+  constexpr int RPB = 256 / LPR;      // rows per workgroup
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + part * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * D + part * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
+      acc = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(b[w] & 0xFFFF0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && part == 0) delta[row] = acc;
+#endif
+}
+
+// ---- dQ: query-major, K/V tiles streamed through two-slot rings ----
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
+bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+              const float* __restrict__ lse, const float* __restrict__ delta,
+              uint16_t* __restrict__ dq, int N, int BH, int nqb, float c, float scale,
+              int causal_arg) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using T = BTile<D>;
+  constexpr int BR = NW * 32;
+  const bool causal = causal_arg != 0;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::TILEB];
+  char* const kring = smem;
+  char* const vring = smem + 2 * T::TILEB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+
+  // work item: whole heads per XCD, heaviest causal query blocks first
+  const int id = static_cast<int>(blockIdx.x);
+  int bh, qb;
+  if (BH % kXcdsB == 0) {
+    const int x = id % kXcdsB, s = id / kXcdsB, hx = BH / kXcdsB;
+    if (causal) { qb = nqb - 1 - s / hx; bh = x + kXcdsB * (s % hx); }
+    else        { bh = x + kXcdsB * (s / nqb); qb = s % nqb; }
+  } else if (causal) {
+    qb = nqb - 1 - id / BH; bh = id % BH;
+  } else {
+    bh = id / nqb; qb = id % nqb;
+  }
+  const int q0 = qb * BR, q0w = q0 + wave * 32, qrow = q0w + j;
+  const int64_t base = static_cast<int64_t>(bh) * N * D;
+  const uint16_t* kbase = k + base;
+  const uint16_t* vbase = v + base;
+
+  const int kend = causal ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + BT - 1) / BT;
+  if (ntiles > 0) {
+    copy_tile<D, NW>(kring, kbase, 0, N, wave, lane);
+    copy_tile<D, NW>(vring, vbase, 0, N, wave, lane);
+  }
+  // this lane's Q and dO row as B operands (rows past N read as zero)
+  bf16x8 qr[D / 16], dor[D / 16];
+  {
+    const int rows = max(0, min(32, N - q0w));
+    const int64_t r0 = base + static_cast<int64_t>(min(q0w, N)) * D;
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(q + r0), 0, rows * T::ROWB, 0x00020000);
+    const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dout + r0), 0, rows * T::ROWB, 0x00020000);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int off = j * T::ROWB + (ks * 16 + 8 * h) * 2;
+      qr[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      dor[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
+    }
+  }
+  float lse2 = 0.f, dl = 0.f;
+  if (qrow < N) {
+    lse2 = lse[static_cast<int64_t>(bh) * N + qrow] * kLog2e;
+    dl = delta[static_cast<int64_t>(bh) * N + qrow];
+  }
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  const BLane<D> la(j, h, lane);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const char* kst = kring + (t & 1) * T::TILEB;
+    const char* vst = vring + (t & 1) * T::TILEB;
+    if (t + 1 < ntiles) {
+      copy_tile<D, NW>(kring + ((t + 1) & 1) * T::TILEB, kbase, (t + 1) * BT, N, wave, lane);
+      copy_tile<D, NW>(vring + ((t + 1) & 1) * T::TILEB, vbase, (t + 1) * BT, N, wave, lane);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key0 = t * BT + kb * 32;
+      if (key0 >= N || (causal && key0 > q0w + 31)) continue;   // wave-uniform
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        s = mfma(lds_row(kst + kb * 32 * T::ROWB + la.rofs[ks]), qr[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        dp = mfma(lds_row(vst + kb * 32 * T::ROWB + la.rofs[ks]), dor[ks], dp);
+      // dS^T = P^T (dP^T - D), keys of this lane in accumulator-row order
+      uint32_t dsw[2][4];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float ds[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int key = key0 + 8 * ((r + x) >> 2) + 4 * h + ((r + x) & 3);
+          const bool masked = (key >= N) || (causal && key > qrow);
+          const float p = masked ? 0.f : fast_exp2(fmaf(s[r + x], c, -lse2));
+          ds[x] = p * (dp[r + x] - dl);
+        }
+        dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(ds[0], ds[1]);
+      }
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dsw[cg][0], dsw[cg][1], dsw[cg][2], dsw[cg][3]});
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma(lds_trans<D>(kst, la, db, 2 * kb + cg), dsb, acc[db]);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  if (qrow < N) store_rows<D>(dq + base + static_cast<int64_t>(qrow) * D, acc, h, scale);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---- dK, dV: key-major, K/V of the block in LDS, Q/dO tiles streamed ----
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                const float* __restrict__ lse, const float* __restrict__ delta,
+                uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int BH, int nkb,
+                float c, float scale, int causal_arg) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using T = BTile<D>;
+  constexpr int BK = NW * 32;                  // keys per workgroup
+  constexpr int KVB = BK * T::ROWB;            // bytes of the block's K (or V)
+  constexpr int SB = 2 * BT * 4;               // LSE and D of one query tile
+  static_assert(BK % BT == 0, "key block is whole tiles");
+  const bool causal = causal_arg != 0;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KVB + 4 * T::TILEB + 2 * SB];
+  char* const kt = smem;
+  char* const vt = smem + KVB;
+  char* const qring = smem + 2 * KVB;
+  char* const dring = qring + 2 * T::TILEB;
+  char* const sring = dring + 2 * T::TILEB;    // [slot][LSE BT floats | D BT floats]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+
+  // work item: whole heads per XCD; causal: the first key blocks see the
+  // most query tiles, so they go first
+  const int id = static_cast<int>(blockIdx.x);
+  int bh, kb;
+  if (BH % kXcdsB == 0) {
+    const int x = id % kXcdsB, s = id / kXcdsB, hx = BH / kXcdsB;
+    if (causal) { kb = s / hx; bh = x + kXcdsB * (s % hx); }
+    else        { bh = x + kXcdsB * (s / nkb); kb = s % nkb; }
+  } else if (causal) {
+    kb = id / BH; bh = id % BH;
+  } else {
+    bh = id / nkb; kb = id % nkb;
+  }
+  const int k0 = kb * BK, k0w = k0 + wave * 32, key = k0w + j;
+  const int64_t base = static_cast<int64_t>(bh) * N * D;
+  const int64_t sbase = static_cast<int64_t>(bh) * N;
+  const uint16_t* qbase = q + base;
+  const uint16_t* dbase = dout + base;
+
+  const int nqt = (N + BT - 1) / BT;
+  const int qt0 = causal ? k0 / BT : 0;
+  // K and V of the block, then the first query tile
+#pragma unroll
+  for (int cpy = 0; cpy < BK / BT; ++cpy)
+    if (k0 + cpy * BT < N) {
+      copy_tile<D, NW>(kt + cpy * T::TILEB, k + base, k0 + cpy * BT, N, wave, lane);
+      copy_tile<D, NW>(vt + cpy * T::TILEB, v + base, k0 + cpy * BT, N, wave, lane);
+    }
+  auto copy_qtile = [&](int qt, int slot) {
+    copy_tile<D, NW>(qring + slot * T::TILEB, qbase, qt * BT, N, wave, lane);
+    copy_tile<D, NW>(dring + slot * T::TILEB, dbase, qt * BT, N, wave, lane);
+    if (wave == 0) {
+      const uint32_t bytes = static_cast<uint32_t>(min(BT, N - qt * BT)) * 4u;
+      dma4(uniform_desc(lse + sbase + qt * BT, bytes), sring + slot * SB, lane * 4);
+      dma4(uniform_desc(delta + sbase + qt * BT, bytes), sring + slot * SB + BT * 4, lane * 4);
+    }
+  };
+  if (qt0 < nqt) copy_qtile(qt0, 0);
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) { dka[db] = f32x16{}; dva[db] = f32x16{}; }
+  const BLane<D> la(j, h, lane);
+  const char* kw = kt + wave * 32 * T::ROWB;   // this wave's 32 keys
+  const char* vw = vt + wave * 32 * T::ROWB;
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int slot = (qt - qt0) & 1;
+    const char* qst = qring + slot * T::TILEB;
+    const char* dst = dring + slot * T::TILEB;
+    const char* sst = sring + slot * SB;
+    if (qt + 1 < nqt) copy_qtile(qt + 1, slot ^ 1);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int qs = qt * BT + sb * 32;
+      if (qs >= N || k0w >= N || (causal && qs + 31 < k0w)) continue;   // wave-uniform
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        s = mfma(lds_row(qst + sb * 32 * T::ROWB + la.rofs[ks]), lds_row(kw + la.rofs[ks]), s);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        dp = mfma(lds_row(dst + sb * 32 * T::ROWB + la.rofs[ks]), lds_row(vw + la.rofs[ks]), dp);
+      // P and dS for this lane's key and the 16 queries 8g + 4h + (0..3)
+      uint32_t pw[2][4], dsw[2][4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lg = *reinterpret_cast<const f32x4*>(sst + (sb * 32 + 8 * g + 4 * h) * 4);
+        const f32x4 dg = *reinterpret_cast<const f32x4*>(sst + BT * 4 + (sb * 32 + 8 * g + 4 * h) * 4);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * g + x;
+          const int qq = qs + 8 * g + 4 * h + x;
+          const bool masked = (qq >= N) || (key >= N) || (causal && key > qq);
+          pv[x] = masked ? 0.f : fast_exp2(fmaf(s[r], c, -lg[x] * kLog2e));
+          dsv[x] = pv[x] * (dp[r] - dg[x]);
+        }
+        pw[g >> 1][(g & 1) * 2 + 0] = pack_bf16x2(pv[0], pv[1]);
+        pw[g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+        dsw[g >> 1][(g & 1) * 2 + 0] = pack_bf16x2(dsv[0], dsv[1]);
+        dsw[g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[cg][0], pw[cg][1], pw[cg][2], pw[cg][3]});
+        const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dsw[cg][0], dsw[cg][1], dsw[cg][2], dsw[cg][3]});
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dva[db] = mfma(lds_trans<D>(dst, la, db, 2 * sb + cg), pb, dva[db]);
+          dka[db] = mfma(lds_trans<D>(qst, la, db, 2 * sb + cg), dsb, dka[db]);
+        }
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  if (key < N) {
+    store_rows<D>(dk + base + static_cast<int64_t>(key) * D, dka, h, scale);
+    store_rows<D>(dv + base + static_cast<int64_t>(key) * D, dva, h, 1.f);
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a) {
+  const int BH = a.B * a.H;
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const float c = a.scale * kLog2e;
+  const auto* q = static_cast<const uint16_t*>(a.q);
+  const auto* k = static_cast<const uint16_t*>(a.k);
+  const auto* v = static_cast<const uint16_t*>(a.v);
+  const auto* o = static_cast<const uint16_t*>(a.o);
+  const auto* dout = static_cast<const uint16_t*>(a.dout);
+  const int64_t rows = static_cast<int64_t>(BH) * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)),
+                     dim3(256), 0, st, o, dout, a.delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  constexpr int NWK = 4;                       // dK/dV: 128 keys per workgroup
+  const int nkb = (a.N + NWK * 32 - 1) / (NWK * 32);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWK>), dim3(static_cast<unsigned>(static_cast<int64_t>(nkb) * BH)),
+                     dim3(NWK * 64), 0, st, q, k, v, dout, a.lse, a.delta,
+                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, BH, nkb, c,
+                     a.scale, a.causal);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  constexpr int NWQ = D == 128 ? 8 : 4;        // dQ: as the forward kernel
+  const int nqb = (a.N + NWQ * 32 - 1) / (NWQ * 32);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NWQ>), dim3(static_cast<unsigned>(static_cast<int64_t>(nqb) * BH)),
+                     dim3(NWQ * 64), 0, st, q, k, v, dout, a.lse, a.delta,
+                     static_cast<uint16_t*>(a.dq), a.N, BH, nqb, c, a.scale, a.causal);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a) {
+  return a.d == 64 ? launch_bwd_d<64>(a) : launch_bwd_d<128>(a);
+}
+
+}  // namespace attn127

@@ -48,9 +48,27 @@ struct Fp8PrepArgs {
   void* stream;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;        // caller's scratch, B*H*N floats
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  void* stream;
+};
+
 hipError_t launch_simple(const LaunchArgs& a);
 hipError_t launch_mfma_bf16(const LaunchArgs& a);
 hipError_t launch_fp8_prepare(const Fp8PrepArgs& a);
 hipError_t launch_fp8_fwd(const Fp8Args& a);
+hipError_t launch_bwd(const BwdArgs& a);
 
 }  // namespace attn127

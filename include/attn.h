@@ -1,5 +1,6 @@
 /*
- * attn.h -- C ABI of the fused exact-attention forward library (gfx950).
+ * attn.h -- C ABI of the fused exact-attention library (gfx950): forward,
+ * fp8 forward and backward.
  *
  * The operation (page "Self-Attention, CUDA kernels and FlashAttention",
  * section 1): for every batch b and head h, with Q, K, V the N x d slices
@@ -111,9 +112,10 @@ int attn_fp8_prepare(const float* q, const float* k, const float* v,
 /*
  * attn_fwd_fp8 -- attention on the e4m3 tensors attn_fp8_prepare writes.
  * Value of an input element = decode(code) * scale of its 128-token tile.
- * Both products run on fp8 MFMA with float32 accumulation; P is quantised
- * to e4m3 as the second product's operand; the tile scales of Q, K and V are
- * applied in float32 inside the softmax and the rescale.  o is bf16
+ * Q K^T runs on fp8 MFMA (e4m3 x e4m3, float32 accumulation) with the Q and
+ * K tile scales folded into the exponent's multiplier.  P V runs on bf16
+ * MFMA: each e4m3 V tile is widened to bf16 (exact) in LDS, and P, carrying
+ * the V tile's scale, is rounded to bf16 (nearest-even).  o is bf16
  * [B][H][N][d]; lse (nullable) float32 [B][H][N].  Other conventions as
  * attn_fwd.
  */
@@ -121,6 +123,31 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  const float* q_scale, const float* k_scale,
                  const float* v_scale, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, void* stream);
+
+/*
+ * attn_bwd -- gradients of attn_fwd (page "Self-Attention, CUDA kernels and
+ * FlashAttention", section 3: the backward pass keeps only the per-row
+ * statistic and recomputes the attention tiles on chip).  Given dO, the
+ * gradient of a loss with respect to O, for every head:
+ *
+ *     P = exp(S - LSE)  (recomputed, masked as in the forward pass)
+ *     dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,
+ *     dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
+ *
+ * q, k, v, o, dout: bf16 [B][H][N][d], o and lse exactly as attn_fwd wrote
+ * them for the same q, k, v, scale and causal.  dq, dk, dv: bf16
+ * [B][H][N][d], written.  lse: float32 [B][H][N], read (4-byte aligned).
+ * delta: float32 [B][H][N], the caller's scratch (4-byte aligned), receives D.
+ * All products on bf16 MFMA with float32 accumulation; P and dS rounded to
+ * bf16 (nearest-even) as operands; outputs rounded to bf16.  dtype must be
+ * ATTN_BF16 (ATTN_F32 returns ATTN_ERR_UNSUPPORTED).  Three launches on
+ * `stream`, no atomics: results are deterministic.  Other conventions as
+ * attn_fwd; lse and delta may not be NULL.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* lse, float* delta, void* dq,
+             void* dk, void* dv, int B, int H, int N, int d, float scale,
+             int causal, int dtype, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_strerror(int status);

@@ -24,6 +24,10 @@ Per-head factors multiply both Q and K of head h before any rounding.  An
 outlier channel is multiplied by ``outlier_mult`` for every batch and token.
 bf16 workloads round the float32 draws to bf16 (round to nearest, ties to
 even) and return them as float32 arrays whose values are exactly bf16.
+
+The output gradient dO of the backward pass comes from its own stream,
+``default_rng(SeedSequence([seed, 1]))``: float32 ``standard_normal((B, H, N,
+d))``, rounded the same way for bf16 workloads.
 """
 from __future__ import annotations
 
@@ -32,7 +36,7 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "random_inputs",
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_output_grad", "random_inputs",
            "round_to_bf16_bits", "haar_orthogonal"]
 
 
@@ -145,6 +149,15 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> dict:
         q, k, v = (round_to_bf16_bits(x) for x in (q, k, v))
     out["q"], out["k"], out["v"] = q, k, v
     return out
+
+
+def make_output_grad(w: Workload | str, seed: int | None = None) -> np.ndarray:
+    """dO for workload ``w``: float32 ``[B,H,N,d]``, exactly bf16 for bf16 workloads."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed if seed is None else seed, 1]))
+    do = _draw(rng, w.B, w.H, w.N, w.d)
+    return round_to_bf16_bits(do) if w.dtype == "bf16" else do
 
 
 def random_inputs(B, H, N, d, dtype="bf16", causal=False, seed=0, **kw) -> dict:

@@ -78,3 +78,25 @@ def test_fp8_entry_points_validate():
 def test_grid_limit_rejected():
     # B*H*ceil(N/64) would not fit a 1-D grid
     assert _fwd("attn_fwd", B=1 << 15, H=1 << 15, N=64 * 4) == -1
+
+
+def _bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, delta=FAKE, dq=FAKE, dk=FAKE,
+         dv=FAKE, B=1, H=1, N=8, d=128, scale=0.125, causal=0, dtype=1):
+    return A.lib().attn_bwd(q, k, v, o, do, lse, delta, dq, dk, dv, B, H, N, d, scale, causal,
+                            dtype, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(do=None), dict(lse=None),
+    dict(delta=None), dict(dq=None), dict(dk=None), dict(dv=None),
+    dict(do=FAKE + 8), dict(dq=FAKE + 2), dict(lse=FAKE + 2), dict(delta=FAKE + 1),
+    dict(d=96), dict(N=-1), dict(dtype=2), dict(scale=0.0), dict(scale=float("nan")),
+])
+def test_bwd_invalid_arguments_rejected(bad):
+    assert _bwd(**bad) == -1
+
+
+def test_bwd_float32_is_unsupported_and_empty_is_a_noop():
+    assert _bwd(dtype=0) == -2
+    for empty in (dict(B=0), dict(H=0), dict(N=0)):
+        assert _bwd(**empty) == 0
