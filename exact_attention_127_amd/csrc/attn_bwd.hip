@@ -12,8 +12,9 @@
 //   dQ  = scale * dS K,   dK = scale * dS^T Q
 // Nothing N x N reaches memory.  Three launches, no atomics:
 //  * bwd_delta_kernel: D for every row (HBM-bound).
-//  * bwd_dkdv_kernel: one workgroup per (b*h, block of keys); K and V of the
-//    block sit in LDS, Q / dO tiles stream through a two-slot ring.  Each
+//  * bwd_dkdv_kernel: one workgroup per (b*h, block of keys); each wave keeps
+//    its keys' K rows in registers and the block's V sits in LDS; Q / dO
+//    tiles stream through a two-slot ring shared by the workgroup.  Each
 //    wave owns 32 keys, so S = Q K^T and dP = dO V^T are computed with the
 //    key in the accumulator column: every lane holds 16 queries of one key,
 //    which is the B-operand layout that dV^T += dO^T P and dK^T += Q^T dS
@@ -297,9 +298,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// ---- dK, dV: key-major, K/V of the block in LDS, Q/dO tiles streamed ----
+// ---- dK, dV: key-major; each wave's K and V rows in registers, Q/dO tiles streamed ----
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                 const float* __restrict__ lse, const float* __restrict__ delta,
@@ -308,14 +309,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = BTile<D>;
   constexpr int BK = NW * 32;                  // keys per workgroup
-  constexpr int KVB = BK * T::ROWB;            // bytes of the block's K (or V)
   constexpr int SB = 2 * BT * 4;               // LSE and D of one query tile
-  static_assert(BK % BT == 0, "key block is whole tiles");
   const bool causal = causal_arg != 0;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * KVB + 4 * T::TILEB + 2 * SB];
-  char* const kt = smem;
-  char* const vt = smem + KVB;
-  char* const qring = smem + 2 * KVB;
+  constexpr int VB = BK * T::ROWB;             // V rows of the block
+  static_assert(BK % BT == 0, "key block is whole tiles");
+  __shared__ __attribute__((aligned(1024))) char smem[VB + 4 * T::TILEB + 2 * SB];
+  char* const vt = smem;
+  char* const qring = smem + VB;
   char* const dring = qring + 2 * T::TILEB;
   char* const sring = dring + 2 * T::TILEB;    // [slot][LSE BT floats | D BT floats]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
@@ -341,13 +341,23 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   const int nqt = (N + BT - 1) / BT;
   const int qt0 = causal ? k0 / BT : 0;
-  // K and V of the block, then the first query tile
+  // V of the block into LDS; this lane's K row (key k0w + j) as B operands
+  // (rows past N read as zero)
 #pragma unroll
   for (int cpy = 0; cpy < BK / BT; ++cpy)
-    if (k0 + cpy * BT < N) {
-      copy_tile<D, NW>(kt + cpy * T::TILEB, k + base, k0 + cpy * BT, N, wave, lane);
-      copy_tile<D, NW>(vt + cpy * T::TILEB, v + base, k0 + cpy * BT, N, wave, lane);
+    if (k0 + cpy * BT < N) copy_tile<D, NW>(vt + cpy * T::TILEB, v + base, k0 + cpy * BT, N, wave, lane);
+  bf16x8 kr[D / 16];
+  {
+    const int rows = max(0, min(32, N - k0w));
+    const int64_t r0 = base + static_cast<int64_t>(min(k0w, N)) * D;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + r0), 0, rows * T::ROWB, 0x00020000);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int off = j * T::ROWB + (ks * 16 + 8 * h) * 2;
+      kr[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     }
+  }
+  const char* vw = vt + wave * 32 * T::ROWB;   // this wave's 32 V rows
   auto copy_qtile = [&](int qt, int slot) {
     copy_tile<D, NW>(qring + slot * T::TILEB, qbase, qt * BT, N, wave, lane);
     copy_tile<D, NW>(dring + slot * T::TILEB, dbase, qt * BT, N, wave, lane);
@@ -362,8 +372,6 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) { dka[db] = f32x16{}; dva[db] = f32x16{}; }
   const BLane<D> la(j, h, lane);
-  const char* kw = kt + wave * 32 * T::ROWB;   // this wave's 32 keys
-  const char* vw = vt + wave * 32 * T::ROWB;
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -380,7 +388,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        s = mfma(lds_row(qst + sb * 32 * T::ROWB + la.rofs[ks]), lds_row(kw + la.rofs[ks]), s);
+        s = mfma(lds_row(qst + sb * 32 * T::ROWB + la.rofs[ks]), kr[ks], s);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
         dp = mfma(lds_row(dst + sb * 32 * T::ROWB + la.rofs[ks]), lds_row(vw + la.rofs[ks]), dp);
@@ -442,7 +450,7 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  constexpr int NWK = 4;                       // dK/dV: 128 keys per workgroup
+  constexpr int NWK = D == 128 ? 8 : 4;        // dK/dV: 256 (d=128) or 128 keys per workgroup
   const int nkb = (a.N + NWK * 32 - 1) / (NWK * 32);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWK>), dim3(static_cast<unsigned>(static_cast<int64_t>(nkb) * BH)),
                      dim3(NWK * 64), 0, st, q, k, v, dout, a.lse, a.delta,
