@@ -1,9 +1,12 @@
-"""Benchmark: fused exact attention forward on one MI355X.
+"""Benchmark: fused exact attention on one MI355X.
 
 One step = one forward call over the whole workload (every head, every
 query block, the full key loop), inputs resident in device memory.  The
 default workload is the long-sequence causal case B=1, H=16, N=16384,
 d=128, bf16.  Throughput counts 4*B*H*N^2*d FLOPs, halved for causal.
+``--pass bwd`` times one backward call (attn_bwd: dQ, dK, dV from the
+forward's O and LSE and a seeded dO) instead, counted as 2.5 times the
+forward's FLOPs.
 
 Prints one JSON line per workload.  ``roofline`` compares the kernel's rate
 (HIP events around the timed launches, on the launch stream) with the
@@ -31,7 +34,13 @@ KERNEL_SOURCES = {
     "fp8": ["exact_attention_127_amd/csrc/attn_fp8.hip",
             "exact_attention_127_amd/csrc/device_util.h",
             "exact_attention_127_amd/csrc/common.h"],
+    "bwd": ["exact_attention_127_amd/csrc/attn_bwd.hip",
+            "exact_attention_127_amd/csrc/device_util.h",
+            "exact_attention_127_amd/csrc/common.h"],
 }
+# the backward's products: dV, dP, dQ, dK and the recomputed S, each the size of
+# one forward product, i.e. 2.5 times the forward's algorithmic FLOPs
+BWD_FLOP_FACTOR = 2.5
 
 
 def kernel_hash(kind: str) -> str:
@@ -83,6 +92,35 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
                       f"{dt:.1f} s"}
 
 
+def cpu_baseline_bwd(inp, do, budget_s: float = 12.0) -> dict:
+    """The float64 gradient oracle on whole heads until ~budget_s elapse."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = inp["workload"]
+    flops_head = algorithmic_flops(w, "bwd") / (w.B * w.H)
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            oracle.attention_backward_head(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
+                                           do[b, h], inp["scale"], w.causal)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * flops_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} heads (dQ, dK, dV of all {w.N} rows each), "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
 def timed(step, stream, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -106,10 +144,17 @@ def timed(step, stream, steps, warmup):
 
 
 def algorithmic_bytes(w, kind: str) -> int:
-    """Q, K, V read once (2 B per element in bf16, 1 B in fp8), O (bf16) and
-    LSE (float32) written once."""
+    """Forward: Q, K, V read once (2 B per element in bf16, 1 B in fp8), O
+    (bf16) and LSE (float32) written once.  Backward: Q, K, V, O, dO and LSE
+    read once, dQ, dK, dV written once, the row statistic D written and read."""
+    if kind == "bwd":
+        return w.B * w.H * w.N * (5 * 2 * w.d + 4 + 3 * 2 * w.d + 8)
     in_bytes = 2 if kind == "bf16" else 1
     return w.B * w.H * w.N * (3 * in_bytes * w.d + 2 * w.d + 4)
+
+
+def algorithmic_flops(w, kind: str) -> float:
+    return w.flops * (BWD_FLOP_FACTOR if kind == "bwd" else 1.0)
 
 
 def roofline(w, kind: str, kernel_ms: float, peak_tflops: float):
@@ -117,11 +162,12 @@ def roofline(w, kind: str, kernel_ms: float, peak_tflops: float):
     its algorithmic bytes at peak bandwidth takes longer than its FLOPs at
     peak matrix-core rate, else the matrix cores."""
     alg_bytes = algorithmic_bytes(w, kind)
-    if alg_bytes / (HBM_PEAK_GBS * 1e9) > w.flops / (peak_tflops * 1e12):
+    flops = algorithmic_flops(w, kind)
+    if alg_bytes / (HBM_PEAK_GBS * 1e9) > flops / (peak_tflops * 1e12):
         roof = {"bound": "hbm", "achieved": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": round(w.flops / (kernel_ms * 1e-3) / 1e12, 2),
+        roof = {"bound": "mfma", "achieved": round(flops / (kernel_ms * 1e-3) / 1e12, 2),
                 "peak": round(peak_tflops, 1), "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     return roof, alg_bytes
@@ -137,7 +183,23 @@ def run_workload(name, args):
     inp = make_inputs(w)
     stream = torch.cuda.current_stream()
     extra = {}
-    if w.dtype == "bf16":
+    if args.pass_ == "bwd":
+        if w.dtype != "bf16":
+            raise SystemExit(f"the backward pass takes bf16 workloads, not {name}")
+        from seeded_inputs import make_output_grad
+        kind = "bwd"
+        q, k, v = (torch.from_numpy(inp[x]).to(dev).to(torch.bfloat16).contiguous() for x in "qkv")
+        do_np = make_output_grad(w)
+        dout = torch.from_numpy(do_np).to(dev).to(torch.bfloat16).contiguous()
+        o, lse = A.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, stream=stream)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        delta = torch.empty_like(lse)
+
+        def step():
+            A.attn_bwd(q, k, v, o, dout, lse, dq=dq, dk=dk, dv=dv, delta=delta, scale=w.scale,
+                       causal=w.causal, stream=stream)
+        peak = PEAK["bf16"]
+    elif w.dtype == "bf16":
         kind = "bf16"
         q, k, v = (torch.from_numpy(inp[x]).to(dev).to(torch.bfloat16).contiguous() for x in "qkv")
         o = torch.empty_like(q)
@@ -167,24 +229,27 @@ def run_workload(name, args):
         raise SystemExit(f"bench.py times the bf16 and fp8 workloads, not {name}")
 
     ms_per_step, kernel_ms = timed(step, stream, args.steps, args.warmup)
-    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    flops = algorithmic_flops(w, kind)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
     roof, alg_bytes = roofline(w, kind, kernel_ms, peak)
     line = {
-        "metric": "attn fwd TFLOP/s + % of bf16 MFMA peak, B=1 H=16 N=16384 d=128 causal"
-        if name == "long_causal_16k" else f"attn fwd TFLOP/s, {name}",
+        "metric": ("attn fwd TFLOP/s + % of bf16 MFMA peak, B=1 H=16 N=16384 d=128 causal"
+                   if name == "long_causal_16k" and kind != "bwd" else
+                   f"attn {'bwd' if kind == 'bwd' else 'fwd'} TFLOP/s, {name}"),
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "seed": w.seed, "flops_per_step": w.flops,
+                   "causal": w.causal, "seed": w.seed, "flops_per_step": flops,
+                   "pass": "bwd" if kind == "bwd" else "fwd",
                    "pct_of_peak": round(100 * tflops / peak, 2)},
-        "roofline": {**roof, "traffic": traffic_from_profile(w.name, kind),
+        "roofline": {**roof, "traffic": traffic_from_profile(w.name + ("_bwd" if kind == "bwd" else ""), kind),
                      "algorithmic_bytes": alg_bytes,
                      "kernel_ms": round(kernel_ms, 4), "kernel_hash": kernel_hash(kind)},
     }
     line.update(extra)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp)
+        line["cpu_baseline"] = cpu_baseline_bwd(inp, do_np) if kind == "bwd" else cpu_baseline(inp)
     print(json.dumps(line), flush=True)
 
 
@@ -195,6 +260,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal_16k",
                     help="workload name, or 'all' for one line per bf16/fp8 workload")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward pass (default) or the backward pass (bf16 workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB per step (counter calibration)")
@@ -216,7 +283,8 @@ def main() -> int:
                           "launches": args.warmup + args.steps}))
         return 0
     names = ([args.workload] if args.workload != "all" else
-             ["long_causal_16k", "vit_b16_batch64", "llm_layer_4k", "fp8_outliers_8k"])
+             ["long_causal_16k", "vit_b16_batch64", "llm_layer_4k"] +
+             ([] if args.pass_ == "bwd" else ["fp8_outliers_8k"]))
     for n in names:
         run_workload(n, args)
     return 0

@@ -79,3 +79,20 @@ def test_cpu_baseline_reports_the_oracle_sample():
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
     assert r["sample"].startswith("1 of 2 heads (all 64 query rows each)")
+
+
+def test_backward_is_counted_as_two_and_a_half_forwards():
+    w = WORKLOADS["long_causal_16k"]
+    assert bench.algorithmic_flops(w, "bwd") == 2.5 * w.flops
+    assert bench.algorithmic_bytes(w, "bwd") == 16 * 16384 * (10 * 128 + 4 + 6 * 128 + 8)
+    roof, _ = bench.roofline(w, "bwd", 1.0, bench.PEAK["bf16"])
+    assert roof["bound"] == "mfma"
+    assert roof["achieved"] == pytest.approx(2.5 * w.flops / 1e-3 / 1e12, rel=1e-3)
+
+
+def test_cpu_baseline_of_the_backward_reports_the_oracle_sample():
+    from seeded_inputs import make_output_grad
+    w = WORKLOADS["long_causal_16k"].with_(B=1, H=2, N=64)
+    r = bench.cpu_baseline_bwd(make_inputs(w), make_output_grad(w), budget_s=0.0)
+    assert r["kind"] == "oracle" and r["value"] > 0
+    assert r["sample"].startswith("1 of 2 heads (dQ, dK, dV of all 64 rows each)")
