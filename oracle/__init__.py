@@ -17,6 +17,9 @@ Sources followed (page title, section):
     section 1, FP8 bullet (block quantisation with an independent scale per
     small tile; incoherent processing: Q and K multiplied by a random
     orthogonal matrix before quantisation).
+  * "Efficient MoE training for biological foundation models", the section
+    on memory and quantisation costs (MXFP8: one scale per block of 32
+    values): ``mx`` holds that block quantisation.
   * The backward pass of the first page, section 3 (only small statistics
     are kept; tiles are recomputed): ``backward`` holds the gradients of the
     forward definition, written out by the chain rule.
@@ -37,9 +40,11 @@ from .formats import (bf16_round, bf16_half_ulp, e4m3_decode, e4m3_encode,
 from .fp8 import fp8_prepare, fp8_dequantize, QUANT_TILE
 from .backward import (attention_backward, attention_backward_head, row_delta,
                        dq_rows, dkdv_cols)
+from .mx import mxfp8_prepare, quantize_mx, dequantize_mx, mx_exponent, MX_BLOCK
 
 __all__ = ["attention", "attention_rows", "attention_probs", "lse_rows",
            "bf16_round", "bf16_half_ulp", "e4m3_decode", "e4m3_encode",
            "E4M3_MAX", "e4m3_table", "fp8_prepare", "fp8_dequantize",
            "QUANT_TILE", "attention_backward", "attention_backward_head",
-           "row_delta", "dq_rows", "dkdv_cols"]
+           "row_delta", "dq_rows", "dkdv_cols", "mxfp8_prepare", "quantize_mx",
+           "dequantize_mx", "mx_exponent", "MX_BLOCK"]
