@@ -11,6 +11,8 @@ The functions keep the C names:
     attn_fwd_simple(...)                       same contract, plain kernel
     attn_fp8_prepare(q, k, v, R)               -> (q8, k8, v8, sq, sk, sv)
     attn_fwd_fp8(q8, k8, v8, sq, sk, sv, ...)  -> (o, lse)
+    attn_mxfp8_prepare(q, k, v, R)             -> (q8, k8, v8, sq, sk, sv)  E8M0 per 32 channels
+    attn_fwd_mxfp8(q8, k8, v8, sq, sk, sv, ...) -> (o, lse)
     attn_bwd(q, k, v, o, dout, lse, ...)       -> (dq, dk, dv)
     attn_strerror(status)
 """
@@ -22,16 +24,18 @@ import os
 
 import torch  # loads the HIP runtime that the library then shares
 
-__all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd",
+__all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
+           "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "MX_BLOCK",
            "attn_strerror", "AttnError", "AttnLibraryMissing", "lib", "LIB_PATH",
            "EXPORTED_SYMBOLS", "ATTN_F32", "ATTN_BF16", "FP8_TILE"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn127.so")
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
-                    "attn_bwd", "attn_strerror")
+                    "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "attn_strerror")
 ATTN_F32, ATTN_BF16 = 0, 1
 FP8_TILE = 128
+MX_BLOCK = 32
 _STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
            -3: "ATTN_ERR_HIP"}
 
@@ -69,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fp8_prepare.restype = _I
         L.attn_fwd_fp8.argtypes = [_P] * 8 + [_I, _I, _I, _I, _F, _I, _P]
         L.attn_fwd_fp8.restype = _I
+        L.attn_mxfp8_prepare.argtypes = [_P] * 10 + [_I, _I, _I, _I, _P]
+        L.attn_mxfp8_prepare.restype = _I
+        L.attn_fwd_mxfp8.argtypes = [_P] * 8 + [_I, _I, _I, _I, _F, _I, _P]
+        L.attn_fwd_mxfp8.restype = _I
         L.attn_bwd.argtypes = [_P] * 10 + [_I, _I, _I, _I, _F, _I, _I, _P]
         L.attn_bwd.restype = _I
         L.attn_strerror.argtypes = [_I]
@@ -207,3 +215,42 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, scale
                         int(bool(causal)), ATTN_BF16, _stream(stream))
     _check(st, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_mxfp8_prepare(q, k, v, R, stream=None):
+    """MXFP8 codes and E8M0 scale bytes ([B, H, N, d/32] uint8) of q R, k R and v."""
+    B, H, N, d = q.shape
+    for t in (q, k, v):
+        if t.shape != q.shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous float32 [B, H, N, d]")
+    if R.shape != (d, d) or R.dtype != torch.float32 or not R.is_contiguous():
+        raise ValueError("R must be contiguous float32 [d, d]")
+    codes = [torch.empty((B, H, N, d), dtype=torch.uint8, device=q.device) for _ in range(3)]
+    scales = [torch.empty((B, H, N, d // MX_BLOCK), dtype=torch.uint8, device=q.device) for _ in range(3)]
+    st = lib().attn_mxfp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(R), *(_ptr(c) for c in codes),
+                                  *(_ptr(s) for s in scales), B, H, N, d, _stream(stream))
+    _check(st, "attn_mxfp8_prepare")
+    return (*codes, *scales)
+
+
+def attn_fwd_mxfp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, scale=None, causal=False,
+                   stream=None, with_lse=True):
+    """Attention on MXFP8 codes with E8M0 block scales; O is bf16."""
+    B, H, N, d = q8.shape
+    for t in (q8, k8, v8):
+        if t.shape != q8.shape or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 [B, H, N, d]")
+    for s_ in (sq, sk, sv):
+        if s_.shape != (B, H, N, d // MX_BLOCK) or s_.dtype != torch.uint8 or not s_.is_contiguous():
+            raise ValueError("scales must be contiguous uint8 [B, H, N, d/32]")
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_fwd_mxfp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv),
+                              _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+                              _stream(stream))
+    _check(st, "attn_fwd_mxfp8")
+    return o, lse

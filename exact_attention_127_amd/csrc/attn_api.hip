@@ -53,6 +53,43 @@ int fwd_common(bool simple, const void* q, const void* k, const void* v, void* o
 
 }  // namespace
 
+namespace {
+int fp8_prepare_common(bool mx, const float* q, const float* k, const float* v, const float* R,
+                       uint8_t* q8, uint8_t* k8, uint8_t* v8, void* q_scale, void* k_scale,
+                       void* v_scale, int B, int H, int N, int d, void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (!q || !k || !v || !R || !q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale)
+    return ATTN_ERR_INVALID_ARG;
+  const void* ps[] = {q, k, v, R, q8, k8, v8};
+  for (const void* p : ps)
+    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  const void* ss[] = {q_scale, k_scale, v_scale};
+  for (const void* p : ss)   // per-tile float scales: 4-byte alignment; E8M0 rows: d/32 bytes
+    if (reinterpret_cast<uintptr_t>(p) & static_cast<uintptr_t>(mx ? (d / 32 - 1) : 3)) return ATTN_ERR_INVALID_ARG;
+  if (st == 1) return ATTN_OK;
+  attn127::Fp8PrepArgs a{q, k, v, R, q8, k8, v8, q_scale, k_scale, v_scale, B, H, N, d, mx ? 1 : 0, stream};
+  return status_of(attn127::launch_fp8_prepare(a));
+}
+
+int fp8_fwd_common(bool mx, const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                   const void* q_scale, const void* k_scale, const void* v_scale, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal, void* stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (check_scale(scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (check_ptrs(q8, k8, v8, o, lse) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
+  const void* ss[] = {q_scale, k_scale, v_scale};
+  for (const void* p : ss)
+    if (reinterpret_cast<uintptr_t>(p) & static_cast<uintptr_t>(mx ? (d / 32 - 1) : 3)) return ATTN_ERR_INVALID_ARG;
+  if (st == 1) return ATTN_OK;
+  attn127::Fp8Args a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale,
+                     causal ? 1 : 0, mx ? 1 : 0, stream};
+  return status_of(attn127::launch_fp8_fwd(a));
+}
+}  // namespace
+
 extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -65,39 +102,31 @@ int attn_fwd_simple(const void* q, const void* k, const void* v, void* o, float*
   return fwd_common(true, q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream);
 }
 
+
 int attn_fp8_prepare(const float* q, const float* k, const float* v, const float* R, uint8_t* q8,
                      uint8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, float* v_scale,
                      int B, int H, int N, int d, void* stream) {
-  int st = check_shape(B, H, N, d);
-  if (st < 0) return st;
-  if (!q || !k || !v || !R || !q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale)
-    return ATTN_ERR_INVALID_ARG;
-  const void* ps[] = {q, k, v, R, q8, k8, v8};
-  for (const void* p : ps)
-    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
-  const void* ss[] = {q_scale, k_scale, v_scale};
-  for (const void* p : ss)
-    if (reinterpret_cast<uintptr_t>(p) & 3u) return ATTN_ERR_INVALID_ARG;
-  if (st == 1) return ATTN_OK;
-  attn127::Fp8PrepArgs a{q, k, v, R, q8, k8, v8, q_scale, k_scale, v_scale, B, H, N, d, stream};
-  return status_of(attn127::launch_fp8_prepare(a));
+  return fp8_prepare_common(false, q, k, v, R, q8, k8, v8, q_scale, k_scale, v_scale, B, H, N, d, stream);
 }
 
 int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
                  const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, void* stream) {
-  int st = check_shape(B, H, N, d);
-  if (st < 0) return st;
-  if (check_scale(scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
-  if (check_ptrs(q8, k8, v8, o, lse) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
-  if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
-  const void* ss[] = {q_scale, k_scale, v_scale};
-  for (const void* p : ss)
-    if (reinterpret_cast<uintptr_t>(p) & 3u) return ATTN_ERR_INVALID_ARG;
-  if (st == 1) return ATTN_OK;
-  attn127::Fp8Args a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale,
-                     causal ? 1 : 0, stream};
-  return status_of(attn127::launch_fp8_fwd(a));
+  return fp8_fwd_common(false, q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale,
+                        causal, stream);
+}
+
+int attn_mxfp8_prepare(const float* q, const float* k, const float* v, const float* R, uint8_t* q8,
+                       uint8_t* k8, uint8_t* v8, uint8_t* q_scale, uint8_t* k_scale,
+                       uint8_t* v_scale, int B, int H, int N, int d, void* stream) {
+  return fp8_prepare_common(true, q, k, v, R, q8, k8, v8, q_scale, k_scale, v_scale, B, H, N, d, stream);
+}
+
+int attn_fwd_mxfp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const uint8_t* q_scale,
+                   const uint8_t* k_scale, const uint8_t* v_scale, void* o, float* lse, int B, int H,
+                   int N, int d, float scale, int causal, void* stream) {
+  return fp8_fwd_common(true, q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale,
+                        causal, stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -65,12 +65,27 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
 }
 #endif
 
-template <int D>
+#if defined(__HIP_DEVICE_COMPILE__)
+// MXFP8 scale exponent of a block whose largest magnitude is am:
+// e = ceil(log2(am / 448)) clamped to [-127, 127], -127 for am = 0.  With
+// am = 1.m * 2^E (448 = 1.75 * 2^8): e = E - 8, plus one when 1.m > 1.75.
+__device__ __forceinline__ int mx_exponent(float am) {
+  const uint32_t b = __float_as_uint(am);
+  const int et = static_cast<int>((b >> 23) & 0xFFu);
+  if (!(am > 0.f) || et == 0) return -127;          // zero or below 2^-126
+  const int e = (et - 127) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return max(-127, min(127, e));
+}
+#endif
+
+// MX = false: one float32 scale per 128-token tile (s = amax/448).
+// MX = true: one E8M0 byte per 32 channels of each token (scale 2^e).
+template <int D, bool MX>
 __global__ void __launch_bounds__(prep_threads<D>())
 fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
                    const float* __restrict__ v, const float* __restrict__ R,
                    uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, uint8_t* __restrict__ v8,
-                   float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv,
+                   void* __restrict__ sq, void* __restrict__ sk, void* __restrict__ sv,
                    int N, int BH, int ntq) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int TP = kTile8 + 4;                 // token stride of the transposed tile (16-byte rows)
@@ -86,7 +101,7 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
   const int bh = id / ntq, tile = id % ntq;
   const float* src = tensor == 0 ? q : (tensor == 1 ? k : v);
   uint8_t* dst = tensor == 0 ? q8 : (tensor == 1 ? k8 : v8);
-  float* scale_out = tensor == 0 ? sq : (tensor == 1 ? sk : sv);
+  void* scale_out = tensor == 0 ? sq : (tensor == 1 ? sk : sv);
   const bool rotate = tensor < 2;
   const int t0 = tile * kTile8;
   const int rows = min(kTile8, N - t0);
@@ -135,6 +150,31 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[r][c] = xt[(cc + c) * TP + tt + r];
   }
+  if constexpr (MX) {
+    // per token: the 32-channel block is 4 adjacent lanes of 8 channels
+    uint8_t* sc = static_cast<uint8_t*>(scale_out);
+    const int blk = cc / 32;
+#pragma unroll
+    for (int r = 0; r < TT; ++r) {
+      float am = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(y[r][c]));
+      am = fmaxf(am, __shfl_xor(am, 1));
+      am = fmaxf(am, __shfl_xor(am, 2));
+      const int e = mx_exponent(am);
+      if (tt + r >= rows) continue;
+      const float inv = ldexpf(1.f, -e);         // exact power of two
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lo |= e4m3_encode(y[r][c] * inv) << (8 * c);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) hi |= e4m3_encode(y[r][c + 4] * inv) << (8 * c);
+      *reinterpret_cast<u32x2*>(dst + off + static_cast<int64_t>(tt + r) * D + cc) = u32x2{lo, hi};
+      if ((cc & 31) == 0)
+        sc[(static_cast<int64_t>(bh) * N + t0 + tt + r) * (D / 32) + blk] = static_cast<uint8_t>(e + 127);
+    }
+    return;
+  }
   // amax over the tile (padding rows are zero)
   float am = 0.f;
 #pragma unroll
@@ -148,7 +188,7 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
   for (int w = 1; w < kPrepThreads / 64; ++w) am = fmaxf(am, red[w]);
   const float s = am > 0.f ? am / kE4m3Max : 1.f;
-  if (tid == 0) scale_out[static_cast<int64_t>(bh) * ntq + tile] = s;
+  if (tid == 0) static_cast<float*>(scale_out)[static_cast<int64_t>(bh) * ntq + tile] = s;
 #pragma unroll
   for (int r = 0; r < TT; ++r) {
     if (tt + r >= rows) break;
@@ -215,22 +255,35 @@ __device__ __forceinline__ void issue_copy8(char* dst, const uint8_t* src, int k
 
 // The blocks of a V tile this wave copied: e4m3 codes -> bf16 (exact), into
 // the bf16 tile.  Lane i's 16 codes are channels 16c..16c+15 of one row.
+// Row and channel chunk (16 codes) that lane `lane` converts in block b.
 template <int D>
-__device__ __forceinline__ void convert_v(char* dst16, const char* src8, int wave, int lane) {
+__device__ __forceinline__ void convert_slot(int wave, int lane, int b, int& row, int& c) {
+  using C = Cfg8<D>;
+  const int blk = wave * C::BPW + b;
+  row = blk * C::RPB + lane / C::CPR;
+  c = (lane % C::CPR) ^ swz8<D>(row);
+}
+
+// vscale[b]: the power of two multiplying block b's codes (1 for per-tile
+// scales, whose factor rides on P; 2^e of the 32-channel block for MXFP8).
+template <int D>
+__device__ __forceinline__ void convert_v(char* dst16, const char* src8, int wave, int lane,
+                                          const float (&vscale)[Cfg8<D>::BPW]) {
   using C = Cfg8<D>;
 #pragma unroll
   for (int b = 0; b < C::BPW; ++b) {
     const int blk = wave * C::BPW + b;
-    const int row = blk * C::RPB + lane / C::CPR;
-    const int c = (lane % C::CPR) ^ swz8<D>(row);
+    int row, c;
+    convert_slot<D>(wave, lane, b, row, c);
     const u32x4 x = *reinterpret_cast<const u32x4*>(src8 + blk * 1024 + lane * 16);
+    const float sc = vscale[b];
     u32x4 lo, hi;
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
-      lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
-      hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], 1.0f, false));
-      hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], 1.0f, true));
+      lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], sc, false));
+      lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], sc, true));
+      hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], sc, false));
+      hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], sc, true));
     }
     char* r16 = dst16 + row * C::ROWB16;
     *reinterpret_cast<u32x4*>(r16 + (((2 * c) ^ swz16<D>(row)) << 4)) = lo;
@@ -242,17 +295,36 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   // operand formats 0/0 = e4m3; block scales 127 = 2^0
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// Block-scaled form: each lane's 32 codes of A (B) are multiplied by
+// 2^(sa-127) (2^(sb-127)); sa, sb are E8M0 bytes in bits 7:0.
+__device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// E8M0 bytes of one token row (D/32 of them, packed little-endian) from a
+// [rows][D/32] byte array; rows past the descriptor's range read as zero.
+template <int D>
+__device__ __forceinline__ uint32_t load_row_scales(__amdgpu_buffer_rsrc_t r, int row) {
+  if constexpr (D == 128) return __builtin_amdgcn_raw_buffer_load_b32(r, row * 4, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b16(r, row * 2, 0, 0);
+}
 #endif
 
 // Scores on fp8 MFMA; P V on bf16 MFMA with V^ converted exactly to bf16 and
 // the V tile scale carried by P (p * s_v rounded to bf16: the same relative
 // rounding as the bf16 kernel's P, where e4m3 P would lose up to 2^-4 of
 // each weight).
-template <int D, bool CAUSAL>
+//
+// MX = true (MXFP8): every token row carries one E8M0 scale per 32 channels.
+// The score MFMA applies the K and Q block scales itself (each lane's 32
+// codes are one block), V is widened to bf16 with its block scale (exact),
+// and P carries no scale.  Each lane loads the scale bytes it needs with the
+// tile copies, so they are covered by the same wait.
+template <int D, bool CAUSAL, bool MX>
 __global__ void __launch_bounds__(NT8, 2)
 attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
-                const uint8_t* __restrict__ v8, const float* __restrict__ sq,
-                const float* __restrict__ sk, const float* __restrict__ sv,
+                const uint8_t* __restrict__ v8, const void* __restrict__ sqv,
+                const void* __restrict__ skv, const void* __restrict__ svv,
                 uint16_t* __restrict__ o, float* __restrict__ lse, int N, int BH, int nqb,
                 int ntq, float c0) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -287,10 +359,41 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   const int64_t base = static_cast<int64_t>(bh) * N * D;
   const uint8_t* kbase = k8 + base;
   const uint8_t* vbase = v8 + base;
-  const float* skh = sk + static_cast<int64_t>(bh) * ntq;
-  const float* svh = sv + static_cast<int64_t>(bh) * ntq;
-  // exponent multiplier without the key tile's scale: s_q * scale * log2(e)
-  const float cq = c0 * sq[static_cast<int64_t>(bh) * ntq + q0 / kTile8];
+  // per-tile scales: the key tile's and value tile's scale and the
+  // multiplier s_q * scale * log2(e); MXFP8: per-head scale arrays
+  const float* skh = MX ? nullptr : static_cast<const float*>(skv) + static_cast<int64_t>(bh) * ntq;
+  const float* svh = MX ? nullptr : static_cast<const float*>(svv) + static_cast<int64_t>(bh) * ntq;
+  const float cq = MX ? c0 : c0 * static_cast<const float*>(sqv)[static_cast<int64_t>(bh) * ntq + q0 / kTile8];
+  constexpr int SPR = D / 32;                    // scale bytes per row (MXFP8)
+  const int64_t sbase = static_cast<int64_t>(bh) * N * SPR;
+  const auto rks = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(skv) + (MX ? sbase : 0)), 0, MX ? N * SPR : 0, 0x00020000);
+  const auto rvs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(svv) + (MX ? sbase : 0)), 0, MX ? N * SPR : 0, 0x00020000);
+  uint32_t kscw[2] = {0u, 0u};                   // this lane's K row scales, current tile
+  float vsc[Cfg8<D>::BPW];                       // V block scales of the tile being converted
+  auto load_tile_scales = [&](int kv0n, uint32_t (&kw)[2], float (&vs)[Cfg8<D>::BPW]) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kw[kb] = load_row_scales<D>(rks, kv0n + kb * 32 + j);
+#pragma unroll
+      for (int b = 0; b < Cfg8<D>::BPW; ++b) {
+        int row, cch;
+        convert_slot<D>(wave, lane, b, row, cch);
+        const uint32_t e = __builtin_amdgcn_raw_buffer_load_b8(rvs, (kv0n + row) * SPR + cch / 2, 0, 0);
+        vs[b] = static_cast<float>(e);           // exponent byte; widened after the wait
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < Cfg8<D>::BPW; ++b) vs[b] = 1.f;
+    }
+  };
+  auto widen = [&](float (&vs)[Cfg8<D>::BPW]) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int b = 0; b < Cfg8<D>::BPW; ++b) vs[b] = ldexpf(1.f, static_cast<int>(vs[b]) - 127);
+    }
+  };
 
   const int kend = CAUSAL ? min(N, q0 + BR8) : N;
   const int ntiles = (kend + BC8 - 1) / BC8;
@@ -299,6 +402,18 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
 
   issue_copy8<D>(kring, kbase, 0, N, wave, lane);
   issue_copy8<D>(vstage, vbase, 0, N, wave, lane);
+  load_tile_scales(0, kscw, vsc);
+  // Q block scales of this lane's row, k-step ks: block 2 ks + h
+  int qsc[D / 64];
+  {
+    uint32_t qw = 0u;
+    if constexpr (MX) {
+      if (qrow < N) qw = D == 128 ? *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(sqv) + sbase + static_cast<int64_t>(qrow) * SPR)
+                                  : *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(sqv) + sbase + static_cast<int64_t>(qrow) * SPR);
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) qsc[ks] = static_cast<int>((qw >> (8 * (2 * ks + h))) & 0xFFu);
+  }
 
   // Q^ as the B operand: k-step ks holds channels ks*64 + 32h .. +31
   i32x8 qr[D / 64];
@@ -308,14 +423,22 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
         const_cast<uint8_t*>(q8 + base + static_cast<int64_t>(min(q0w, N)) * D), 0, rows * D, 0x00020000);
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks) {
-      const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rq, j * D + ks * 64 + 32 * h, 0, 0);
-      const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rq, j * D + ks * 64 + 32 * h + 16, 0, 0);
+      // MXFP8: the block-scaled instruction takes a lane's bytes 0-15 into
+      // the k-step's first 32-channel block and bytes 16-31 into the second
+      // (each block scaled by the low / high half-wave's scale), so a lane
+      // holds channels 16h..+15 and 32+16h..+15 of the step.  Per-tile
+      // scales are uniform over the step and keep 32 contiguous channels.
+      const int lo_c = MX ? ks * 64 + 16 * h : ks * 64 + 32 * h;
+      const int hi_c = MX ? ks * 64 + 32 + 16 * h : ks * 64 + 32 * h + 16;
+      const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rq, j * D + lo_c, 0, 0);
+      const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rq, j * D + hi_c, 0, 0);
       qr[ks] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
                      static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
     }
   }
   wait_vmcnt<0>();
-  convert_v<D>(vring, vstage, wave, lane);     // this wave's own copied blocks
+  widen(vsc);
+  convert_v<D>(vring, vstage, wave, lane, vsc);     // this wave's own copied blocks
   __syncthreads();
 
   f32x16 oacc[D / 32];
@@ -339,9 +462,11 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
     const int kv0 = t * BC8;
     const char* kst = kring + (t & 1) * C::TILEB;
     const char* vst = vring + (t & 1) * C::TILEB16;
+    uint32_t kscw_next[2] = {0u, 0u};
     if (t + 1 < ntiles) {
       issue_copy8<D>(kring + ((t + 1) & 1) * C::TILEB, kbase, kv0 + BC8, N, wave, lane);
       issue_copy8<D>(vstage, vbase, kv0 + BC8, N, wave, lane);
+      load_tile_scales(kv0 + BC8, kscw_next, vsc);
     }
     if (t <= last) {
       // ---- S^T = K^ Q^^T, two 32-key blocks ----
@@ -352,12 +477,16 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
         const char* krow = kst + (kb * 32 + j) * C::ROWB;
 #pragma unroll
         for (int ks = 0; ks < D / 64; ++ks) {
-          const int c0i = 4 * ks + 2 * h;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + ((c0i ^ ksw) << 4));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + (((c0i + 1) ^ ksw) << 4));
+          const int clo = MX ? 4 * ks + h : 4 * ks + 2 * h;          // 16-byte chunks, as for Q
+          const int chi = MX ? 4 * ks + 2 + h : 4 * ks + 2 * h + 1;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + ((clo ^ ksw) << 4));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + ((chi ^ ksw) << 4));
           const i32x8 a = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
                                 static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
-          sacc[kb] = mfma_fp8(a, qr[ks], sacc[kb]);
+          if constexpr (MX)
+            sacc[kb] = mfma_mx(a, qr[ks], sacc[kb], static_cast<int>((kscw[kb] >> (8 * (2 * ks + h))) & 0xFFu), qsc[ks]);
+          else
+            sacc[kb] = mfma_fp8(a, qr[ks], sacc[kb]);
         }
       }
       // ---- masks ----
@@ -372,7 +501,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
           }
       }
       // ---- online softmax; the key tile's scale enters the multiplier ----
-      const float ct = cq * skh[kv0 / kTile8];
+      const float ct = MX ? cq : cq * skh[kv0 / kTile8];
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -389,8 +518,8 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
       }
       // operand p' = p * s_v = exp2(s*ct - m + log2 s_v); the normaliser
       // takes sum(p') / s_v
-      const float svt = svh[kv0 / kTile8];
-      const float mref = ((m == -INFINITY) ? 0.f : m) - __log2f(svt);
+      const float svt = MX ? 1.f : svh[kv0 / kTile8];
+      const float mref = ((m == -INFINITY) ? 0.f : m) - (MX ? 0.f : __log2f(svt));
       uint32_t pw[4][4];
       float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -403,7 +532,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
           ls1 += p1;
           pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
         }
-      lsum += (ls0 + ls1) / svt;
+      lsum += MX ? (ls0 + ls1) : (ls0 + ls1) / svt;
       // ---- O^T += V^T P'^T (bf16) ----
 #pragma unroll
       for (int c16 = 0; c16 < 4; ++c16) {
@@ -422,7 +551,10 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
       // its V blocks into the free bf16 slot (tile t-1's, read before the
       // previous barrier)
       wait_vmcnt<0>();
-      convert_v<D>(vring + ((t + 1) & 1) * C::TILEB16, vstage, wave, lane);
+      widen(vsc);
+      convert_v<D>(vring + ((t + 1) & 1) * C::TILEB16, vstage, wave, lane, vsc);
+      kscw[0] = kscw_next[0];
+      kscw[1] = kscw_next[1];
     }
     __syncthreads();
   }
@@ -447,24 +579,24 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D>
+template <int D, bool MX>
 hipError_t prep_one(const Fp8PrepArgs& a) {
   const int BH = a.B * a.H;
   const int ntq = (a.N + kTile8 - 1) / kTile8;
   const int64_t blocks = 3LL * BH * ntq;
-  hipLaunchKernelGGL((fp8_prepare_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(prep_threads<D>()), 0,
+  hipLaunchKernelGGL((fp8_prepare_kernel<D, MX>), dim3(static_cast<unsigned>(blocks)), dim3(prep_threads<D>()), 0,
                      static_cast<hipStream_t>(a.stream), a.q, a.k, a.v, a.R, a.q8, a.k8, a.v8,
                      a.sq, a.sk, a.sv, a.N, BH, ntq);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MX>
 hipError_t fwd_one(const Fp8Args& a) {
   const int BH = a.B * a.H;
   const int nqb = (a.N + BR8 - 1) / BR8;
   const int ntq = (a.N + kTile8 - 1) / kTile8;
   const int64_t blocks = static_cast<int64_t>(nqb) * BH;
-  hipLaunchKernelGGL((attn_fp8_kernel<D, CAUSAL>), dim3(static_cast<unsigned>(blocks)), dim3(NT8), 0,
+  hipLaunchKernelGGL((attn_fp8_kernel<D, CAUSAL, MX>), dim3(static_cast<unsigned>(blocks)), dim3(NT8), 0,
                      static_cast<hipStream_t>(a.stream), a.q8, a.k8, a.v8, a.sq, a.sk, a.sv,
                      static_cast<uint16_t*>(a.o), a.lse, a.N, BH, nqb, ntq, a.scale * kLog2e);
   return hipGetLastError();
@@ -473,12 +605,17 @@ hipError_t fwd_one(const Fp8Args& a) {
 }  // namespace
 
 hipError_t launch_fp8_prepare(const Fp8PrepArgs& a) {
-  return a.d == 64 ? prep_one<64>(a) : prep_one<128>(a);
+  if (a.mx) return a.d == 64 ? prep_one<64, true>(a) : prep_one<128, true>(a);
+  return a.d == 64 ? prep_one<64, false>(a) : prep_one<128, false>(a);
 }
 
 hipError_t launch_fp8_fwd(const Fp8Args& a) {
-  if (a.d == 64) return a.causal ? fwd_one<64, true>(a) : fwd_one<64, false>(a);
-  return a.causal ? fwd_one<128, true>(a) : fwd_one<128, false>(a);
+  if (a.mx) {
+    if (a.d == 64) return a.causal ? fwd_one<64, true, true>(a) : fwd_one<64, false, true>(a);
+    return a.causal ? fwd_one<128, true, true>(a) : fwd_one<128, false, true>(a);
+  }
+  if (a.d == 64) return a.causal ? fwd_one<64, true, false>(a) : fwd_one<64, false, false>(a);
+  return a.causal ? fwd_one<128, true, false>(a) : fwd_one<128, false, false>(a);
 }
 
 }  // namespace attn127

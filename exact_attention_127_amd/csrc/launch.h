@@ -22,14 +22,15 @@ struct Fp8Args {
   const uint8_t* q8;
   const uint8_t* k8;
   const uint8_t* v8;
-  const float* sq;
-  const float* sk;
-  const float* sv;
+  const void* sq;      // float32 per 128-token tile, or E8M0 bytes per 32 channels (mx)
+  const void* sk;
+  const void* sv;
   void* o;             // bf16
   float* lse;          // nullable
   int B, H, N, d;
   float scale;
   int causal;
+  int mx;              // 1: MXFP8 (E8M0 scale per 32 channels of a token)
   void* stream;
 };
 
@@ -41,10 +42,11 @@ struct Fp8PrepArgs {
   uint8_t* q8;
   uint8_t* k8;
   uint8_t* v8;
-  float* sq;
-  float* sk;
-  float* sv;
+  void* sq;            // float32 per 128-token tile, or E8M0 bytes per 32 channels (mx)
+  void* sk;
+  void* sv;
   int B, H, N, d;
+  int mx;
   void* stream;
 };
 

@@ -1,6 +1,6 @@
 /*
  * attn.h -- C ABI of the fused exact-attention library (gfx950): forward,
- * fp8 forward and backward.
+ * fp8 and MXFP8 forward, and backward.
  *
  * The operation (page "Self-Attention, CUDA kernels and FlashAttention",
  * section 1): for every batch b and head h, with Q, K, V the N x d slices
@@ -123,6 +123,41 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  const float* q_scale, const float* k_scale,
                  const float* v_scale, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, void* stream);
+
+/* Channels per MXFP8 block: one E8M0 scale per (b, h, token, block). */
+#define ATTN_MX_BLOCK 32
+
+/*
+ * attn_mxfp8_prepare -- MXFP8 block quantisation (page "Efficient MoE
+ * training for biological foundation models", the section on memory and
+ * quantisation costs: 8-bit values with one scale per block of 32 values)
+ * after the same incoherent processing as attn_fp8_prepare (q' = q R,
+ * k' = k R; v not rotated).  For every token and every 32 consecutive
+ * channels: e = ceil(log2(amax / 448)) clamped to [-127, 127] (e = -127 when
+ * amax = 0), scale byte = e + 127 (E8M0), code = e4m3(x / 2^e) (OCP E4M3FN,
+ * nearest-even; no saturation occurs since amax / 2^e <= 448).
+ *
+ * q, k, v: float32 [B][H][N][d].  q8, k8, v8: uint8 codes [B][H][N][d].
+ * q_scale, k_scale, v_scale: uint8 [B][H][N][d/32], aligned to d/32 bytes.
+ */
+int attn_mxfp8_prepare(const float* q, const float* k, const float* v,
+                       const float* R, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                       uint8_t* q_scale, uint8_t* k_scale, uint8_t* v_scale,
+                       int B, int H, int N, int d, void* stream);
+
+/*
+ * attn_fwd_mxfp8 -- attention on the MXFP8 tensors attn_mxfp8_prepare
+ * writes.  Value of an element = decode(code) * 2^(scale byte - 127) of its
+ * 32-channel block.  Q K^T runs on the block-scaled fp8 MFMA, which applies
+ * the Q and K block scales (every lane's 32 codes form one block); P V runs on
+ * bf16 MFMA with each V block widened to bf16 with its scale (exact) and P
+ * rounded to bf16.  o is bf16 [B][H][N][d]; lse (nullable) float32 [B][H][N].
+ * Other conventions as attn_fwd.
+ */
+int attn_fwd_mxfp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                   const uint8_t* q_scale, const uint8_t* k_scale,
+                   const uint8_t* v_scale, void* o, float* lse, int B, int H,
+                   int N, int d, float scale, int causal, void* stream);
 
 /*
  * attn_bwd -- gradients of attn_fwd (page "Self-Attention, CUDA kernels and

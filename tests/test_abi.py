@@ -100,3 +100,18 @@ def test_bwd_float32_is_unsupported_and_empty_is_a_noop():
     assert _bwd(dtype=0) == -2
     for empty in (dict(B=0), dict(H=0), dict(N=0)):
         assert _bwd(**empty) == 0
+
+
+def test_mxfp8_entry_points_validate():
+    L = A.lib()
+    args = [FAKE] * 10
+    assert L.attn_mxfp8_prepare(*args, 1, 1, 8, 48, None) == -1            # d not 64/128
+    assert L.attn_mxfp8_prepare(*([None] + args[1:]), 1, 1, 8, 64, None) == -1
+    assert L.attn_mxfp8_prepare(*(args[:7] + [FAKE + 1] + args[8:]), 1, 1, 8, 64, None) == -1  # scale rows: 2-byte aligned at d=64
+    assert L.attn_mxfp8_prepare(*(args[:7] + [FAKE + 2] + args[8:]), 1, 1, 8, 128, None) == -1  # 4-byte at d=128
+    assert L.attn_mxfp8_prepare(*args, 0, 1, 8, 64, None) == 0
+    f = [FAKE] * 7 + [None]
+    assert L.attn_fwd_mxfp8(*f, 1, 1, 8, 128, -0.5, 0, None) == -1
+    assert L.attn_fwd_mxfp8(*f, 1, 1, 8, 100, 0.1, 0, None) == -1
+    assert L.attn_fwd_mxfp8(*(f[:3] + [None] + f[4:]), 1, 1, 8, 128, 0.1, 0, None) == -1
+    assert L.attn_fwd_mxfp8(*f, 1, 0, 8, 128, 0.1, 0, None) == 0
