@@ -34,6 +34,9 @@ KERNEL_SOURCES = {
     "fp8": ["exact_attention_127_amd/csrc/attn_fp8.hip",
             "exact_attention_127_amd/csrc/device_util.h",
             "exact_attention_127_amd/csrc/common.h"],
+    "mxfp8": ["exact_attention_127_amd/csrc/attn_fp8.hip",
+              "exact_attention_127_amd/csrc/device_util.h",
+              "exact_attention_127_amd/csrc/common.h"],
     "bwd": ["exact_attention_127_amd/csrc/attn_bwd.hip",
             "exact_attention_127_amd/csrc/device_util.h",
             "exact_attention_127_amd/csrc/common.h"],
@@ -145,12 +148,14 @@ def timed(step, stream, steps, warmup):
 
 def algorithmic_bytes(w, kind: str) -> int:
     """Forward: Q, K, V read once (2 B per element in bf16, 1 B in fp8), O
-    (bf16) and LSE (float32) written once.  Backward: Q, K, V, O, dO and LSE
+    (bf16) and LSE (float32) written once; MXFP8 also reads one scale byte per
+    32 channels of every Q, K and V row.  Backward: Q, K, V, O, dO and LSE
     read once, dQ, dK, dV written once, the row statistic D written and read."""
     if kind == "bwd":
         return w.B * w.H * w.N * (5 * 2 * w.d + 4 + 3 * 2 * w.d + 8)
     in_bytes = 2 if kind == "bf16" else 1
-    return w.B * w.H * w.N * (3 * in_bytes * w.d + 2 * w.d + 4)
+    scale_bytes = 3 * (w.d // 32) if kind == "mxfp8" else 0
+    return w.B * w.H * w.N * (3 * in_bytes * w.d + scale_bytes + 2 * w.d + 4)
 
 
 def algorithmic_flops(w, kind: str) -> float:
@@ -173,7 +178,7 @@ def roofline(w, kind: str, kernel_ms: float, peak_tflops: float):
     return roof, alg_bytes
 
 
-def run_workload(name, args):
+def run_workload(name, args, fp8_scales="tile"):
     import torch
     import exact_attention_127_amd as A
     from seeded_inputs import WORKLOADS, make_inputs
@@ -209,20 +214,23 @@ def run_workload(name, args):
             A.attn_fwd(q, k, v, o=o, lse=lse, scale=w.scale, causal=w.causal, stream=stream)
         peak = PEAK["bf16"]
     elif w.dtype == "fp8":
-        kind = "fp8"
+        mx = fp8_scales == "mx"
+        kind = "mxfp8" if mx else "fp8"
+        prepare = A.attn_mxfp8_prepare if mx else A.attn_fp8_prepare
+        forward = A.attn_fwd_mxfp8 if mx else A.attn_fwd_fp8
         qf, kf, vf = (torch.from_numpy(inp[x]).to(dev).contiguous() for x in "qkv")
         R = torch.from_numpy(inp["R"]).to(dev).contiguous()
-        prep = A.attn_fp8_prepare(qf, kf, vf, R)
-        q8, k8, v8, sq, sk, sv = prep
+        q8, k8, v8, sq, sk, sv = prepare(qf, kf, vf, R)
         o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        _, prep_ms = timed(lambda: A.attn_fp8_prepare(qf, kf, vf, R), stream, 3, 1)
-        prep_bytes = 3 * qf.numel() * 4 + 3 * qf.numel() + 3 * sq.numel() * 4 + R.numel() * 4
+        _, prep_ms = timed(lambda: prepare(qf, kf, vf, R), stream, 3, 1)
+        prep_bytes = (3 * qf.numel() * 4 + 3 * qf.numel() + 3 * sq.numel() * sq.element_size()
+                      + R.numel() * 4)
         extra["prepare"] = {"ms": round(prep_ms, 4), "GB_per_s": round(prep_bytes / prep_ms / 1e6, 1)}
 
         def step():
-            A.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, o=o, lse=lse, scale=w.scale, causal=w.causal,
-                           stream=stream)
+            forward(q8, k8, v8, sq, sk, sv, o=o, lse=lse, scale=w.scale, causal=w.causal,
+                    stream=stream)
         # scores on fp8, P V on bf16: time-weighted peak of the two halves
         peak = 1.0 / (0.5 / PEAK["fp8"] + 0.5 / PEAK["bf16"])
     else:
@@ -235,15 +243,17 @@ def run_workload(name, args):
     line = {
         "metric": ("attn fwd TFLOP/s + % of bf16 MFMA peak, B=1 H=16 N=16384 d=128 causal"
                    if name == "long_causal_16k" and kind != "bwd" else
-                   f"attn {'bwd' if kind == 'bwd' else 'fwd'} TFLOP/s, {name}"),
+                   f"attn {'bwd' if kind == 'bwd' else 'fwd'} TFLOP/s, {name}"
+                   + (", MXFP8 scales" if kind == "mxfp8" else "")),
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "seed": w.seed, "flops_per_step": flops,
                    "pass": "bwd" if kind == "bwd" else "fwd",
+                   **({"fp8_scales": fp8_scales} if w.dtype == "fp8" else {}),
                    "pct_of_peak": round(100 * tflops / peak, 2)},
-        "roofline": {**roof, "traffic": traffic_from_profile(w.name + ("_bwd" if kind == "bwd" else ""), kind),
+        "roofline": {**roof, "traffic": traffic_from_profile(w.name + {"bwd": "_bwd", "mxfp8": "_mx"}.get(kind, ""), kind),
                      "algorithmic_bytes": alg_bytes,
                      "kernel_ms": round(kernel_ms, 4), "kernel_hash": kernel_hash(kind)},
     }
@@ -262,6 +272,9 @@ def main() -> int:
                     help="workload name, or 'all' for one line per bf16/fp8 workload")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward pass (default) or the backward pass (bf16 workloads)")
+    ap.add_argument("--fp8-scales", choices=("tile", "mx"), default="tile",
+                    help="fp8 workloads: one float32 scale per 64-row tile (default) or one "
+                         "power-of-two scale per 32 channels of a token (MXFP8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB per step (counter calibration)")
@@ -282,11 +295,14 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2,
                           "launches": args.warmup + args.steps}))
         return 0
-    names = ([args.workload] if args.workload != "all" else
-             ["long_causal_16k", "vit_b16_batch64", "llm_layer_4k"] +
-             ([] if args.pass_ == "bwd" else ["fp8_outliers_8k"]))
-    for n in names:
-        run_workload(n, args)
+    if args.workload != "all":
+        runs = [(args.workload, args.fp8_scales)]
+    else:
+        runs = [(n, "tile") for n in ("long_causal_16k", "vit_b16_batch64", "llm_layer_4k")]
+        if args.pass_ == "fwd":
+            runs += [("fp8_outliers_8k", "tile"), ("fp8_outliers_8k", "mx")]
+    for n, fmt in runs:
+        run_workload(n, args, fmt)
     return 0
 
 
