@@ -59,6 +59,9 @@ int fp8_prepare_common(bool mx, const float* q, const float* k, const float* v, 
                        void* v_scale, int B, int H, int N, int d, void* stream) {
   int st = check_shape(B, H, N, d);
   if (st < 0) return st;
+  // work items (tensor, b*h, 128-token tile) are indexed in 32 bits
+  if (3 * static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 127) / 128) >= (int64_t(1) << 30))
+    return ATTN_ERR_INVALID_ARG;
   if (!q || !k || !v || !R || !q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale)
     return ATTN_ERR_INVALID_ARG;
   const void* ps[] = {q, k, v, R, q8, k8, v8};

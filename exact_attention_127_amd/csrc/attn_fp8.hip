@@ -1,5 +1,5 @@
-// fp8 (OCP e4m3) path: block quantisation with incoherent processing, and
-// the fused attention forward on fp8 matrix cores (gfx950).
+// fp8 (OCP e4m3) path: the fused attention forward on fp8 matrix cores
+// (gfx950); the quantisation that feeds it is in attn_fp8_prepare.hip.
 //
 // Page "FlashAttention scaling, multi-GPU training and weight quantization",
 // section 1, the FP8 bullet: low-precision matrix units double the matmul
@@ -7,11 +7,6 @@
 // independent scale for each small tile (block quantisation) and
 // multiplying Q and K by a random orthogonal matrix first (incoherent
 // processing), which leaves Q K^T unchanged.
-//
-// attn_fp8_prepare: per (tensor, batch*head, tile of 128 tokens) one
-// workgroup loads the tile, rotates it (Q and K: x R in float32), takes the
-// tile's largest magnitude, sets s = amax/448 and writes e4m3(x/s) with
-// nearest-even rounding and saturation.
 //
 // attn_fwd_fp8: the bf16 kernel's structure (transposed scores, in-register
 // online softmax, deferred normalisation, HBM -> LDS copies) with the scores
@@ -33,174 +28,7 @@
 namespace attn127 {
 namespace {
 
-constexpr int kTile8 = 128;          // tokens per quantisation tile
-constexpr float kE4m3Max = 448.0f;
-
-// ---------------------------------------------------------------------------
-// prepare
-// ---------------------------------------------------------------------------
-// 4*d threads: each computes 4 tokens x 8 channels of the rotated tile
-template <int D>
-constexpr int prep_threads() { return 4 * D; }
-
-#if defined(__HIP_DEVICE_COMPILE__)
-// Nearest e4m3 (E4M3FN) code of x: ties to even, |x| >= 448 saturates to
-// 448, NaN -> 0x7F.  Normal range: fp32 mantissa rounded to 3 bits at bit
-// 20, exponent rebiased 127 -> 7; below 2^-6 the spacing is 2^-9.
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  if (x != x) return 0x7Fu;
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  uint32_t code;
-  if (a >= kE4m3Max) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {
-    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // 0..8 (8 = 2^-6)
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    code = (b >> 20) - (120u << 3);
-  }
-  return sign | code;
-}
-#endif
-
-#if defined(__HIP_DEVICE_COMPILE__)
-// MXFP8 scale exponent of a block whose largest magnitude is am:
-// e = ceil(log2(am / 448)) clamped to [-127, 127], -127 for am = 0.  With
-// am = 1.m * 2^E (448 = 1.75 * 2^8): e = E - 8, plus one when 1.m > 1.75.
-__device__ __forceinline__ int mx_exponent(float am) {
-  const uint32_t b = __float_as_uint(am);
-  const int et = static_cast<int>((b >> 23) & 0xFFu);
-  if (!(am > 0.f) || et == 0) return -127;          // zero or below 2^-126
-  const int e = (et - 127) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-  return max(-127, min(127, e));
-}
-#endif
-
-// MX = false: one float32 scale per 128-token tile (s = amax/448).
-// MX = true: one E8M0 byte per 32 channels of each token (scale 2^e).
-template <int D, bool MX>
-__global__ void __launch_bounds__(prep_threads<D>())
-fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                   const float* __restrict__ v, const float* __restrict__ R,
-                   uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, uint8_t* __restrict__ v8,
-                   void* __restrict__ sq, void* __restrict__ sk, void* __restrict__ sv,
-                   int N, int BH, int ntq) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int TP = kTile8 + 4;                 // token stride of the transposed tile (16-byte rows)
-  __shared__ __attribute__((aligned(16))) float xt[D * TP];   // x^T: xt[c*TP + token]
-  __shared__ __attribute__((aligned(16))) float rs[D * D];    // R row-major
-  constexpr int kPrepThreads = prep_threads<D>();
-  __shared__ float red[kPrepThreads / 64];
-
-  const int tid = threadIdx.x;
-  int id = static_cast<int>(blockIdx.x);
-  const int tensor = id / (BH * ntq);
-  id -= tensor * BH * ntq;
-  const int bh = id / ntq, tile = id % ntq;
-  const float* src = tensor == 0 ? q : (tensor == 1 ? k : v);
-  uint8_t* dst = tensor == 0 ? q8 : (tensor == 1 ? k8 : v8);
-  void* scale_out = tensor == 0 ? sq : (tensor == 1 ? sk : sv);
-  const bool rotate = tensor < 2;
-  const int t0 = tile * kTile8;
-  const int rows = min(kTile8, N - t0);
-  const int64_t off = (static_cast<int64_t>(bh) * N + t0) * D;
-
-  for (int e = tid; e < kTile8 * D; e += kPrepThreads) {
-    const int r = e / D, col = e % D;
-    xt[col * TP + r] = (r < rows) ? src[off + static_cast<int64_t>(r) * D + col] : 0.f;
-  }
-  if (rotate)
-    for (int e = tid * 4; e < D * D; e += kPrepThreads * 4)
-      *reinterpret_cast<f32x4*>(rs + e) = *reinterpret_cast<const f32x4*>(R + e);
-  __syncthreads();
-
-  // each thread: TT tokens x 8 channels
-  constexpr int CG = D / 8;                      // channel groups
-  constexpr int TT = kTile8 * CG / kPrepThreads; // tokens per thread (4)
-  static_assert(TT % 4 == 0, "tokens per thread come in 16-byte groups");
-  const int cc = (tid % CG) * 8;
-  const int tt = (tid / CG) * TT;
-  float y[TT][8];
-  if (rotate) {
-#pragma unroll
-    for (int r = 0; r < TT; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) y[r][c] = 0.f;
-    for (int i = 0; i < D; ++i) {
-      float a[TT], b[8];
-#pragma unroll
-      for (int r = 0; r < TT; r += 4) {
-        const f32x4 x4 = *reinterpret_cast<const f32x4*>(xt + i * TP + tt + r);
-        a[r] = x4[0]; a[r + 1] = x4[1]; a[r + 2] = x4[2]; a[r + 3] = x4[3];
-      }
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(rs + i * D + cc);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(rs + i * D + cc + 4);
-      b[0] = b0[0]; b[1] = b0[1]; b[2] = b0[2]; b[3] = b0[3];
-      b[4] = b1[0]; b[5] = b1[1]; b[6] = b1[2]; b[7] = b1[3];
-#pragma unroll
-      for (int r = 0; r < TT; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) y[r][c] = fmaf(a[r], b[c], y[r][c]);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < TT; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) y[r][c] = xt[(cc + c) * TP + tt + r];
-  }
-  if constexpr (MX) {
-    // per token: the 32-channel block is 4 adjacent lanes of 8 channels
-    uint8_t* sc = static_cast<uint8_t*>(scale_out);
-    const int blk = cc / 32;
-#pragma unroll
-    for (int r = 0; r < TT; ++r) {
-      float am = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(y[r][c]));
-      am = fmaxf(am, __shfl_xor(am, 1));
-      am = fmaxf(am, __shfl_xor(am, 2));
-      const int e = mx_exponent(am);
-      if (tt + r >= rows) continue;
-      const float inv = ldexpf(1.f, -e);         // exact power of two
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) lo |= e4m3_encode(y[r][c] * inv) << (8 * c);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) hi |= e4m3_encode(y[r][c + 4] * inv) << (8 * c);
-      *reinterpret_cast<u32x2*>(dst + off + static_cast<int64_t>(tt + r) * D + cc) = u32x2{lo, hi};
-      if ((cc & 31) == 0)
-        sc[(static_cast<int64_t>(bh) * N + t0 + tt + r) * (D / 32) + blk] = static_cast<uint8_t>(e + 127);
-    }
-    return;
-  }
-  // amax over the tile (padding rows are zero)
-  float am = 0.f;
-#pragma unroll
-  for (int r = 0; r < TT; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(y[r][c]));
-  for (int s = 32; s > 0; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
-  if ((tid & 63) == 0) red[tid >> 6] = am;
-  __syncthreads();
-  am = red[0];
-#pragma unroll
-  for (int w = 1; w < kPrepThreads / 64; ++w) am = fmaxf(am, red[w]);
-  const float s = am > 0.f ? am / kE4m3Max : 1.f;
-  if (tid == 0) static_cast<float*>(scale_out)[static_cast<int64_t>(bh) * ntq + tile] = s;
-#pragma unroll
-  for (int r = 0; r < TT; ++r) {
-    if (tt + r >= rows) break;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) lo |= e4m3_encode(y[r][c] / s) << (8 * c);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) hi |= e4m3_encode(y[r][c + 4] / s) << (8 * c);
-    *reinterpret_cast<u32x2*>(dst + off + static_cast<int64_t>(tt + r) * D + cc) = u32x2{lo, hi};
-  }
-#endif  // __HIP_DEVICE_COMPILE__
-}
+constexpr int kTile8 = kFp8Tile;     // tokens per quantisation tile
 
 // ---------------------------------------------------------------------------
 // forward
@@ -579,17 +407,6 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool MX>
-hipError_t prep_one(const Fp8PrepArgs& a) {
-  const int BH = a.B * a.H;
-  const int ntq = (a.N + kTile8 - 1) / kTile8;
-  const int64_t blocks = 3LL * BH * ntq;
-  hipLaunchKernelGGL((fp8_prepare_kernel<D, MX>), dim3(static_cast<unsigned>(blocks)), dim3(prep_threads<D>()), 0,
-                     static_cast<hipStream_t>(a.stream), a.q, a.k, a.v, a.R, a.q8, a.k8, a.v8,
-                     a.sq, a.sk, a.sv, a.N, BH, ntq);
-  return hipGetLastError();
-}
-
 template <int D, bool CAUSAL, bool MX>
 hipError_t fwd_one(const Fp8Args& a) {
   const int BH = a.B * a.H;
@@ -603,11 +420,6 @@ hipError_t fwd_one(const Fp8Args& a) {
 }
 
 }  // namespace
-
-hipError_t launch_fp8_prepare(const Fp8PrepArgs& a) {
-  if (a.mx) return a.d == 64 ? prep_one<64, true>(a) : prep_one<128, true>(a);
-  return a.d == 64 ? prep_one<64, false>(a) : prep_one<128, false>(a);
-}
 
 hipError_t launch_fp8_fwd(const Fp8Args& a) {
   if (a.mx) {

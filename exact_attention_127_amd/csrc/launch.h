@@ -5,6 +5,10 @@
 
 namespace attn127 {
 
+// Tokens per fp8 quantisation tile (one float32 scale per (b, h, tile)),
+// shared by the prepare and the forward kernels.
+constexpr int kFp8Tile = 128;
+
 struct LaunchArgs {
   const void* q;
   const void* k;

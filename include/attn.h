@@ -103,6 +103,9 @@ int attn_fwd_simple(const void* q, const void* k, const void* v, void* o,
  *
  * q, k, v: float32 [B][H][N][d].  q8, k8, v8: uint8 codes [B][H][N][d].
  * q_scale, k_scale, v_scale: float32 [B][H][ceil(N/128)].
+ * The rotation runs on float32 matrix cores (products exact, float32
+ * accumulation).  ATTN_ERR_INVALID_ARG also when 3*B*H*ceil(N/128) >= 2^30
+ * (the work items are indexed in 32 bits; such inputs exceed device memory).
  */
 int attn_fp8_prepare(const float* q, const float* k, const float* v,
                      const float* R, uint8_t* q8, uint8_t* k8, uint8_t* v8,
