@@ -45,7 +45,7 @@ def _check_full(fn, inp, dev, dtype, tol_max=TOL_MAX, tol_mean=TOL_MEAN, tol_lse
     return st
 
 
-SMALL_N = [1, 2, 31, 63, 64, 65, 127, 128, 129, 196, 257, 300]
+SMALL_N = [1, 2, 31, 63, 64, 65, 127, 128, 129, 196, 256, 257, 300]
 
 
 @pytest.mark.parametrize("N", SMALL_N)
