@@ -20,6 +20,9 @@ Sources followed (page title, section):
   * "Efficient MoE training for biological foundation models", the section
     on memory and quantisation costs (MXFP8: one scale per block of 32
     values): ``mx`` holds that block quantisation.
+  * "FlashAttention scaling, multi-GPU training and weight quantization",
+    section 3 (W4A16: packed 4-bit weights unpacked and dequantised to FP16
+    in registers, fed to the matrix units): ``w4a16``.
   * The backward pass of the first page, section 3 (only small statistics
     are kept; tiles are recomputed): ``backward`` holds the gradients of the
     forward definition, written out by the chain rule.
@@ -35,16 +38,18 @@ dK rows sum to zero, the dV rows sum to the dO rows, identical keys give
 dQ = 0).  Every function here is pinned; none is "parity unpinned".
 """
 from .exact import attention, attention_rows, attention_probs, lse_rows
-from .formats import (bf16_round, bf16_half_ulp, e4m3_decode, e4m3_encode,
+from .formats import (bf16_round, bf16_half_ulp, fp16_round, e4m3_decode, e4m3_encode,
                       E4M3_MAX, e4m3_table)
 from .fp8 import fp8_prepare, fp8_dequantize, QUANT_TILE
 from .backward import (attention_backward, attention_backward_head, row_delta,
                        dq_rows, dkdv_cols)
 from .mx import mxfp8_prepare, quantize_mx, dequantize_mx, mx_exponent, MX_BLOCK
+from .w4a16 import unpack_int4, pack_int4, dequantize, w4a16_gemm, w4a16_rows, w4a16_sum_abs
 
 __all__ = ["attention", "attention_rows", "attention_probs", "lse_rows",
            "bf16_round", "bf16_half_ulp", "e4m3_decode", "e4m3_encode",
            "E4M3_MAX", "e4m3_table", "fp8_prepare", "fp8_dequantize",
            "QUANT_TILE", "attention_backward", "attention_backward_head",
            "row_delta", "dq_rows", "dkdv_cols", "mxfp8_prepare", "quantize_mx",
-           "dequantize_mx", "mx_exponent", "MX_BLOCK"]
+           "dequantize_mx", "mx_exponent", "MX_BLOCK", "fp16_round", "unpack_int4",
+           "pack_int4", "dequantize", "w4a16_gemm", "w4a16_rows", "w4a16_sum_abs"]

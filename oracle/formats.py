@@ -2,6 +2,9 @@
 
 * bf16: 1 sign, 8 exponent, 7 fraction bits (float32's exponent range);
   rounding to nearest, ties to the even significand.
+* fp16 (IEEE binary16): 1 sign, 5 exponent bits with bias 15, 10 fraction
+  bits; subnormals m * 2^-24; largest finite value 65504; rounding to
+  nearest, ties to even; magnitudes that round above 65504 become infinite.
 * e4m3 ("E4M3FN" of the OCP 8-bit floating-point specification, the format
   the FP8 bullet of "FlashAttention scaling, multi-GPU training and weight
   quantization", section 1, quantises to): 1 sign, 4 exponent bits with bias
@@ -28,6 +31,21 @@ def bf16_round(x) -> np.ndarray:
     spacing = np.ldexp(1.0, e - 7)
     r = np.rint(ax / spacing) * spacing     # rint: half-way cases go to the even integer
     r = np.where(r > 3.3895313892515355e38, np.inf, r)
+    out[fin] = np.copysign(r, x[fin])
+    return out
+
+
+def fp16_round(x) -> np.ndarray:
+    """Nearest fp16 value of x (float64 in, float64 out), ties to even."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    ax = np.abs(x[fin])
+    _, E = np.frexp(ax)                     # ax in [2^(E-1), 2^E)
+    e = np.maximum(E - 1, -14)              # below 2^-14 the spacing stays 2^-24
+    spacing = np.ldexp(1.0, e - 10)
+    r = np.rint(ax / spacing) * spacing     # rint: half-way cases go to the even integer
+    r = np.where(r > 65504.0, np.inf, r)
     out[fin] = np.copysign(r, x[fin])
     return out
 

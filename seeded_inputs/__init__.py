@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward pass (and the W4A16
+decode product at the end of this file).
 
 This module is shared by the tests, the benchmark and the smoke check.  It
 draws random tensors and nothing else: none of the attention arithmetic
@@ -37,7 +38,8 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "make_output_grad", "random_inputs",
-           "round_to_bf16_bits", "haar_orthogonal"]
+           "round_to_bf16_bits", "haar_orthogonal", "W4Workload", "W4_WORKLOADS",
+           "make_w4a16_inputs"]
 
 
 @dataclass(frozen=True)
@@ -164,3 +166,69 @@ def random_inputs(B, H, N, d, dtype="bf16", causal=False, seed=0, **kw) -> dict:
     """Small ad-hoc workload with the same recipe (used by parity sweeps)."""
     w = Workload(f"adhoc_{B}x{H}x{N}x{d}", B, H, N, d, dtype, causal, seed, **kw)
     return make_inputs(w)
+
+
+# ---------------------------------------------------------------------------
+# W4A16 decode product ("FlashAttention scaling, multi-GPU training and
+# weight quantization", section 3: one token at a time, weights read as 4-bit
+# integers).  The page gives no layer shapes; the workloads take the
+# feed-forward projection of a 70B-class model (hidden size 8192, 28672
+# feed-forward channels) for one token and for a batch of 16 tokens.
+#
+# Recipe (``default_rng(seed)``), in draw order:
+#   1. X: float32 ``standard_normal((M, K))`` cast to fp16 (nearest);
+#   2. packed weights: uint32 ``integers(0, 2**32, (N, K/8))`` -- eight
+#      independent uniform 4-bit integers per word;
+#   3. scales: ``uniform(0.002, 0.02, (N, K/G))`` cast to fp16;
+#   4. zero points: ``integers(4, 12, (N, K/G))`` as uint8.
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class W4Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    G: int
+    seed: int
+    note: str = ""
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+    @property
+    def bytes(self) -> int:
+        """Packed weights, scales (2 B) and zero points (1 B) read once, X read
+        once, Y written once (fp16)."""
+        return (self.N * self.K // 2 + 3 * self.N * (self.K // self.G)
+                + 2 * self.M * self.K + 2 * self.M * self.N)
+
+    def with_(self, **kw) -> "W4Workload":
+        return replace(self, **kw)
+
+
+W4_WORKLOADS = {
+    "w4a16_decode_70b": W4Workload(
+        "w4a16_decode_70b", 1, 28672, 8192, 128, 1101,
+        note="one token through a 70B-class feed-forward projection, int4 groups of 128"),
+    "w4a16_batch16_70b": W4Workload(
+        "w4a16_batch16_70b", 16, 28672, 8192, 128, 1102,
+        note="16 tokens through the same projection"),
+    "w4a16_small": W4Workload(
+        "w4a16_small", 3, 48, 384, 128, 1103, note="small parity case"),
+}
+
+
+def make_w4a16_inputs(w: W4Workload | str, seed: int | None = None) -> dict:
+    """``x`` fp16 [M][K], ``qweight`` uint32 [N][K/8], ``scales`` fp16
+    [N][K/G], ``zeros`` uint8 [N][K/G], and ``G``."""
+    if isinstance(w, str):
+        w = W4_WORKLOADS[w]
+    assert w.K % w.G == 0 and w.K % 8 == 0
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    x = rng.standard_normal((w.M, w.K), dtype=np.float32).astype(np.float16)
+    qweight = rng.integers(0, 2 ** 32, size=(w.N, w.K // 8), dtype=np.uint32)
+    scales = rng.uniform(0.002, 0.02, size=(w.N, w.K // w.G)).astype(np.float16)
+    zeros = rng.integers(4, 12, size=(w.N, w.K // w.G)).astype(np.uint8)
+    return {"workload": w, "x": x, "qweight": qweight, "scales": scales, "zeros": zeros,
+            "G": w.G}
