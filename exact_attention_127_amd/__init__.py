@@ -27,15 +27,18 @@ import torch  # loads the HIP runtime that the library then shares
 __all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
            "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "MX_BLOCK",
            "attn_strerror", "AttnError", "AttnLibraryMissing", "lib", "LIB_PATH",
-           "EXPORTED_SYMBOLS", "ATTN_F32", "ATTN_BF16", "FP8_TILE"]
+           "EXPORTED_SYMBOLS", "ATTN_F32", "ATTN_BF16", "FP8_TILE", "w4a16_gemm",
+           "w4a16_dequantize", "W4A16_GROUP"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn127.so")
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
-                    "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "attn_strerror")
+                    "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "w4a16_gemm",
+                    "w4a16_dequantize", "attn_strerror")
 ATTN_F32, ATTN_BF16 = 0, 1
 FP8_TILE = 128
 MX_BLOCK = 32
+W4A16_GROUP = 128
 _STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
            -3: "ATTN_ERR_HIP"}
 
@@ -79,6 +82,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_mxfp8.restype = _I
         L.attn_bwd.argtypes = [_P] * 10 + [_I, _I, _I, _I, _F, _I, _I, _P]
         L.attn_bwd.restype = _I
+        L.w4a16_gemm.argtypes = [_P] * 5 + [_I, _I, _I, _I, _P]
+        L.w4a16_gemm.restype = _I
+        L.w4a16_dequantize.argtypes = [_P] * 4 + [_I, _I, _I, _P]
+        L.w4a16_dequantize.restype = _I
         L.attn_strerror.argtypes = [_I]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -254,3 +261,45 @@ def attn_fwd_mxfp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, scale=None, causal=
                               _stream(stream))
     _check(st, "attn_fwd_mxfp8")
     return o, lse
+
+
+def _w4_check(qweight, scales, zeros, K, group, device):
+    N = qweight.shape[0]
+    if qweight.dim() != 2 or qweight.element_size() != 4 or qweight.dtype.is_floating_point:
+        raise ValueError("qweight must be a 2-D tensor of 32-bit words [N, K/8]")
+    if tuple(qweight.shape) != (N, K // 8):
+        raise ValueError(f"qweight must be [N, K/8] = [{N}, {K // 8}]")
+    if scales.dtype != torch.float16 or tuple(scales.shape) != (N, K // group):
+        raise ValueError(f"scales must be float16 [N, K/{group}]")
+    if zeros.dtype != torch.uint8 or tuple(zeros.shape) != (N, K // group):
+        raise ValueError(f"zeros must be uint8 [N, K/{group}]")
+    for t in (qweight, scales, zeros):
+        if not t.is_contiguous() or t.device != device:
+            raise ValueError("qweight, scales, zeros must be contiguous and on the same device")
+    return N
+
+
+def w4a16_gemm(x, qweight, scales, zeros, y=None, group=W4A16_GROUP, stream=None):
+    """Y = X W^T, fp16 [M, N], with W dequantised from packed 4-bit words in
+    registers: w = fp16(s * (q - z)) per group of ``group`` k (M <= 16)."""
+    if x.dim() != 2 or x.dtype != torch.float16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float16 [M, K] tensor")
+    M, K = x.shape
+    N = _w4_check(qweight, scales, zeros, K, group, x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    st = lib().w4a16_gemm(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), M, N, K,
+                          int(group), _stream(stream))
+    _check(st, "w4a16_gemm")
+    return y
+
+
+def w4a16_dequantize(qweight, scales, zeros, K, w=None, group=W4A16_GROUP, stream=None):
+    """The fp16 weights [N, K] that w4a16_gemm feeds to the matrix cores."""
+    N = _w4_check(qweight, scales, zeros, K, group, qweight.device)
+    if w is None:
+        w = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
+    st = lib().w4a16_dequantize(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(w), N, K,
+                                int(group), _stream(stream))
+    _check(st, "w4a16_dequantize")
+    return w

@@ -91,6 +91,22 @@ int fp8_fwd_common(bool mx, const uint8_t* q8, const uint8_t* k8, const uint8_t*
                      causal ? 1 : 0, mx ? 1 : 0, stream};
   return status_of(attn127::launch_fp8_fwd(a));
 }
+int w4_check(const void* qweight, const void* scales, const void* zeros, const void* out,
+             int M, int N, int K, int group, bool gemm, const void* x) {
+  if (M < 0 || N < 0 || K < 0) return ATTN_ERR_INVALID_ARG;
+  if (gemm && M > 16) return ATTN_ERR_INVALID_ARG;
+  if (K % 8 != 0) return ATTN_ERR_INVALID_ARG;
+  if (group != 128) return ATTN_ERR_UNSUPPORTED;
+  if (K % group != 0) return ATTN_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(N) * (K / 8) >= (int64_t(1) << 40)) return ATTN_ERR_INVALID_ARG;
+  if (!qweight || !scales || !zeros || !out || (gemm && !x)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(qweight) || (reinterpret_cast<uintptr_t>(scales) & 1u)) return ATTN_ERR_INVALID_ARG;
+  if (gemm ? (!aligned16(x) || (reinterpret_cast<uintptr_t>(out) & 7u)) : !aligned16(out))
+    return ATTN_ERR_INVALID_ARG;
+  if (N == 0 || K == 0 || (gemm && M == 0)) return 1;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,6 +166,22 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   attn127::BwdArgs a{q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale,
                      causal ? 1 : 0, stream};
   return status_of(attn127::launch_bwd(a));
+}
+
+int w4a16_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint8_t* zeros,
+               void* y, int M, int N, int K, int group, void* stream) {
+  const int st = w4_check(qweight, scales, zeros, y, M, N, K, group, true, x);
+  if (st != ATTN_OK) return st == 1 ? ATTN_OK : st;
+  attn127::W4Args a{x, qweight, scales, zeros, y, M, N, K, stream};
+  return status_of(attn127::launch_w4a16(a));
+}
+
+int w4a16_dequantize(const uint32_t* qweight, const void* scales, const uint8_t* zeros, void* w,
+                     int N, int K, int group, void* stream) {
+  const int st = w4_check(qweight, scales, zeros, w, 0, N, K, group, false, nullptr);
+  if (st != ATTN_OK) return st == 1 ? ATTN_OK : st;
+  attn127::W4Args a{nullptr, qweight, scales, zeros, w, 0, N, K, stream};
+  return status_of(attn127::launch_w4a16_dequant(a));
 }
 
 const char* attn_strerror(int status) {

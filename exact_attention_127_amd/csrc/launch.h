@@ -77,4 +77,17 @@ hipError_t launch_fp8_prepare(const Fp8PrepArgs& a);
 hipError_t launch_fp8_fwd(const Fp8Args& a);
 hipError_t launch_bwd(const BwdArgs& a);
 
+struct W4Args {
+  const void* x;           // fp16 [M][K]
+  const uint32_t* qweight; // [N][K/8]
+  const void* scales;      // fp16 [N][K/128]
+  const uint8_t* zeros;    // [N][K/128]
+  void* y;                 // fp16 [M][N] (dequantise: fp16 weights [N][K])
+  int M, N, K;
+  void* stream;
+};
+
+hipError_t launch_w4a16(const W4Args& a);
+hipError_t launch_w4a16_dequant(const W4Args& a);
+
 }  // namespace attn127

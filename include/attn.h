@@ -188,6 +188,43 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int causal, int dtype, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
+/* Weights per scale group of the W4A16 product. */
+#define W4A16_GROUP 128
+
+/*
+ * w4a16_gemm -- Y = X W^T with 4-bit weights dequantised in registers (page
+ * "FlashAttention scaling, multi-GPU training and weight quantization",
+ * section 3: packed INT4 weights read from HBM, unpacked with shifts and
+ * masks, scale and zero point applied to give FP16 values that go straight
+ * to the matrix cores; the expanded weights are never written to memory).
+ *
+ *   w[n][k] = fp16(s[n][k/128] * (q[n][k] - z[n][k/128]))   (rounded once)
+ *   Y[m][n] = fp16(sum_k X[m][k] w[n][k])                    (float32 sums)
+ *
+ * x: fp16 [M][K], 1 <= M <= 16 (tokens of a decode step), 16-byte aligned.
+ * qweight: uint32 [N][K/8]; word (n, j) holds q[n][8j + i] in bits 4i..4i+3;
+ * 16-byte aligned.  scales: fp16 [N][K/128], 2-byte aligned.  zeros: uint8
+ * [N][K/128], values 0..15.  y: fp16 [M][N], 8-byte aligned.
+ * group must be 128 (ATTN_ERR_UNSUPPORTED otherwise); K a multiple of 128.
+ * M, N or K = 0: no-op.  M > 16, a bad size, pointer or alignment:
+ * ATTN_ERR_INVALID_ARG before any HIP call.  Asynchronous on stream;
+ * deterministic (the four K slices of a row block are summed in a fixed
+ * order).  The caller owns all memory; nothing is allocated.
+ */
+int w4a16_gemm(const void* x, const uint32_t* qweight, const void* scales,
+               const uint8_t* zeros, void* y, int M, int N, int K, int group,
+               void* stream);
+
+/*
+ * w4a16_dequantize -- the fp16 weights w[n][k] of w4a16_gemm written out to
+ * w (fp16 [N][K], 16-byte aligned): the unfused path the product avoids,
+ * for checking the dequantisation bit for bit.  Other arguments and errors
+ * as w4a16_gemm.
+ */
+int w4a16_dequantize(const uint32_t* qweight, const void* scales,
+                     const uint8_t* zeros, void* w, int N, int K, int group,
+                     void* stream);
+
 const char* attn_strerror(int status);
 
 #ifdef __cplusplus

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:attn|w4a16)_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_binding_names():
@@ -115,3 +115,24 @@ def test_mxfp8_entry_points_validate():
     assert L.attn_fwd_mxfp8(*f, 1, 1, 8, 100, 0.1, 0, None) == -1
     assert L.attn_fwd_mxfp8(*(f[:3] + [None] + f[4:]), 1, 1, 8, 128, 0.1, 0, None) == -1
     assert L.attn_fwd_mxfp8(*f, 1, 0, 8, 128, 0.1, 0, None) == 0
+
+
+def test_w4a16_entry_points_validate():
+    L = A.lib()
+    g = lambda x=FAKE, q=FAKE, s=FAKE, z=FAKE, y=FAKE, M=1, N=32, K=256, group=128: \
+        L.w4a16_gemm(x, q, s, z, y, M, N, K, group, None)
+    assert g(M=17) == -1                      # more than 16 tokens
+    assert g(M=-1) == -1 and g(N=-1) == -1
+    assert g(K=100) == -1                     # not whole words
+    assert g(K=136) == -1                     # not whole groups
+    assert g(group=64) == -2                  # only groups of 128
+    assert g(x=None) == -1 and g(y=None) == -1 and g(z=None) == -1
+    assert g(q=FAKE + 4) == -1                # words: 16-byte aligned
+    assert g(x=FAKE + 8) == -1                # activations: 16-byte aligned
+    assert g(y=FAKE + 4) == -1                # output: 8-byte aligned
+    assert g(s=FAKE + 1) == -1                # fp16 scales: 2-byte aligned
+    assert g(M=0) == 0 and g(N=0) == 0 and g(K=0) == 0
+    d = lambda q=FAKE, s=FAKE, z=FAKE, w=FAKE, N=32, K=256, group=128: \
+        L.w4a16_dequantize(q, s, z, w, N, K, group, None)
+    assert d(w=FAKE + 8) == -1 and d(K=120) == -1 and d(group=32) == -2
+    assert d(N=0) == 0
