@@ -38,6 +38,8 @@ KERNEL_SOURCES = {
     "mxfp8": ["exact_attention_127_amd/csrc/attn_fp8.hip",
               "exact_attention_127_amd/csrc/device_util.h",
               "exact_attention_127_amd/csrc/common.h"],
+    "w4a16": ["exact_attention_127_amd/csrc/w4a16.hip",
+              "exact_attention_127_amd/csrc/common.h"],
     "bwd": ["exact_attention_127_amd/csrc/attn_bwd.hip",
             "exact_attention_127_amd/csrc/device_util.h",
             "exact_attention_127_amd/csrc/common.h"],
@@ -275,6 +277,79 @@ def run_workload(name, args, fp8_scales="tile"):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_w4(inp, budget_s: float = 12.0) -> dict:
+    """The float64 W4A16 oracle on blocks of output columns until ~budget_s elapse."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = inp["workload"]
+    cols_per = 512
+    t0 = time.perf_counter()
+    done = 0
+    while done < w.N and time.perf_counter() - t0 < budget_s:
+        cols = np.arange(done, min(w.N, done + cols_per))
+        oracle.w4a16_rows(inp["x"], inp["qweight"], inp["scales"], inp["zeros"], w.G, cols)
+        done += len(cols)
+    dt = time.perf_counter() - t0
+    bytes_done = w.bytes * done / w.N
+    return {"value": bytes_done / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.N} output columns (all {w.M} tokens), float64 numpy, {dt:.1f} s"}
+
+
+def run_w4(name, args):
+    """One launch of w4a16_gemm per step; HBM-bound, so the buffers cycle
+    through copies totalling more than 512 MB."""
+    import numpy as np
+    import torch
+    import exact_attention_127_amd as A
+    from seeded_inputs import W4_WORKLOADS, make_w4a16_inputs
+
+    w = W4_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    inp = make_w4a16_inputs(w)
+    stream = torch.cuda.current_stream()
+    base = (torch.from_numpy(inp["x"]).to(dev),
+            torch.from_numpy(inp["qweight"].view(np.int32)).to(dev),
+            torch.from_numpy(inp["scales"]).to(dev),
+            torch.from_numpy(inp["zeros"]).to(dev),
+            torch.empty((w.M, w.N), dtype=torch.float16, device=dev))
+    n_sets = -(-INPUT_SET_BYTES // w.bytes)
+    bufs = [base] + [tuple(t.clone() for t in base) for _ in range(n_sets - 1)]
+    turn = [0]
+
+    def step():
+        x, q, sc, z, y = bufs[turn[0] % len(bufs)]
+        turn[0] += 1
+        A.w4a16_gemm(x, q, sc, z, y=y, group=w.G, stream=stream)
+
+    ms_per_step, kernel_ms = timed(step, stream, args.steps, args.warmup)
+    gbs = w.bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = w.bytes / (kernel_ms * 1e-3) / 1e9
+    line = {
+        "metric": f"w4a16 decode product GB/s (algorithmic bytes), {name}",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4 weights, fp16 activations",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "group": w.G, "seed": w.seed,
+                   "bytes_per_step": w.bytes, "flops_per_step": w.flops, "input_sets": len(bufs),
+                   "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(w.name, "w4a16"),
+                     "algorithmic_bytes": w.bytes, "kernel_ms": round(kernel_ms, 4),
+                     "kernel_hash": kernel_hash("w4a16")},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_w4(inp)
+    print(json.dumps(line), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,9 +387,15 @@ def main() -> int:
     else:
         runs = [(n, "tile") for n in ("long_causal_16k", "vit_b16_batch64", "llm_layer_4k")]
         if args.pass_ == "fwd":
-            runs += [("fp8_outliers_8k", "tile"), ("fp8_outliers_8k", "mx")]
+            runs += [("fp8_outliers_8k", "tile"), ("fp8_outliers_8k", "mx"),
+                     ("w4a16_decode_70b", None), ("w4a16_batch16_70b", None)]
     for n, fmt in runs:
-        run_workload(n, args, fmt)
+        if n.startswith("w4a16"):
+            if args.pass_ == "bwd":
+                raise SystemExit("the W4A16 product has no backward pass here")
+            run_w4(n, args)
+        else:
+            run_workload(n, args, fmt)
     return 0
 
 

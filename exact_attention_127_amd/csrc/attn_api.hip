@@ -97,8 +97,11 @@ int w4_check(const void* qweight, const void* scales, const void* zeros, const v
   if (gemm && M > 16) return ATTN_ERR_INVALID_ARG;
   if (K % 8 != 0) return ATTN_ERR_INVALID_ARG;
   if (group != 128) return ATTN_ERR_UNSUPPORTED;
+  if (K > 32768) return ATTN_ERR_UNSUPPORTED;   // the groups' scales of 32 rows stay in 32 KB of LDS
   if (K % group != 0) return ATTN_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(N) * (K / 8) >= (int64_t(1) << 40)) return ATTN_ERR_INVALID_ARG;
+  // packed weights and activations are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(N) * (K / 2) >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(K) * 2 * 16 >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
   if (!qweight || !scales || !zeros || !out || (gemm && !x)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(qweight) || (reinterpret_cast<uintptr_t>(scales) & 1u)) return ATTN_ERR_INVALID_ARG;
   if (gemm ? (!aligned16(x) || (reinterpret_cast<uintptr_t>(out) & 7u)) : !aligned16(out))

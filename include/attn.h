@@ -205,7 +205,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * qweight: uint32 [N][K/8]; word (n, j) holds q[n][8j + i] in bits 4i..4i+3;
  * 16-byte aligned.  scales: fp16 [N][K/128], 2-byte aligned.  zeros: uint8
  * [N][K/128], values 0..15.  y: fp16 [M][N], 8-byte aligned.
- * group must be 128 (ATTN_ERR_UNSUPPORTED otherwise); K a multiple of 128.
+ * group must be 128 and K at most 32768 (ATTN_ERR_UNSUPPORTED otherwise);
+ * K a multiple of 128;
+ * the packed weights below 2 GiB (N*K/2 < 2^31) and K < 2^26.
  * M, N or K = 0: no-op.  M > 16, a bad size, pointer or alignment:
  * ATTN_ERR_INVALID_ARG before any HIP call.  Asynchronous on stream;
  * deterministic (the four K slices of a row block are summed in a fixed

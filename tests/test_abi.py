@@ -126,6 +126,7 @@ def test_w4a16_entry_points_validate():
     assert g(K=100) == -1                     # not whole words
     assert g(K=136) == -1                     # not whole groups
     assert g(group=64) == -2                  # only groups of 128
+    assert g(K=32768 + 128) == -2             # scales of 32 rows must fit 32 KB of LDS
     assert g(x=None) == -1 and g(y=None) == -1 and g(z=None) == -1
     assert g(q=FAKE + 4) == -1                # words: 16-byte aligned
     assert g(x=FAKE + 8) == -1                # activations: 16-byte aligned

@@ -70,6 +70,16 @@ def test_gemm_matches_the_oracle(gpu, M, N, K):
     assert np.all(err <= bound), (float((err / bound).max()), M, N, K)
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 64, 28672), (5, 40, 32768), (16, 72, 4096), (4, 64, 28672)])
+def test_gemm_long_rows(gpu, M, N, K):
+    # long weight rows: 224 and 256 groups (the staged scales near their LDS
+    # limit, and the launch's choice between 2 and 4 row tiles per wave)
+    inp = _case(M, N, K, M + N + K)
+    y = _gemm(inp, gpu)
+    err, bound, ref = _gate(y, inp)
+    assert np.all(err <= bound), (float((err / bound).max()), M, N, K)
+
+
 def test_one_hot_selects_a_weight_column(gpu):
     inp = _case(4, 40, 512, 3)
     K = 512
