@@ -193,7 +193,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
               const float* __restrict__ lse, const float* __restrict__ delta,
               uint16_t* __restrict__ dq, int N, int BH, int nqb, float c, float scale,
-              int causal_arg) {
+              int causal_arg, int hc) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = BTile<D>;
   constexpr int BR = NW * 32;
@@ -207,9 +207,13 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int id = static_cast<int>(blockIdx.x);
   int bh, qb;
   if (BH % kXcdsB == 0) {
-    const int x = id % kXcdsB, s = id / kXcdsB, hx = BH / kXcdsB;
-    if (causal) { qb = nqb - 1 - s / hx; bh = x + kXcdsB * (s % hx); }
-    else        { bh = x + kXcdsB * (s / nqb); qb = s % nqb; }
+    const int x = id % kXcdsB, s = id / kXcdsB;
+    if (causal) {   // chunks of hc heads, each chunk's blocks heaviest first
+      const int per = hc * nqb, ch = s / per, r = s - ch * per;
+      qb = nqb - 1 - r / hc; bh = x + kXcdsB * (ch * hc + r % hc);
+    } else {
+      bh = x + kXcdsB * (s / nqb); qb = s % nqb;
+    }
   } else if (causal) {
     qb = nqb - 1 - id / BH; bh = id % BH;
   } else {
@@ -305,7 +309,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                 const float* __restrict__ lse, const float* __restrict__ delta,
                 uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int BH, int nkb,
-                float c, float scale, int causal_arg) {
+                float c, float scale, int causal_arg, int hc) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = BTile<D>;
   constexpr int BK = NW * 32;                  // keys per workgroup
@@ -325,9 +329,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int id = static_cast<int>(blockIdx.x);
   int bh, kb;
   if (BH % kXcdsB == 0) {
-    const int x = id % kXcdsB, s = id / kXcdsB, hx = BH / kXcdsB;
-    if (causal) { kb = s / hx; bh = x + kXcdsB * (s % hx); }
-    else        { bh = x + kXcdsB * (s / nkb); kb = s % nkb; }
+    const int x = id % kXcdsB, s = id / kXcdsB;
+    if (causal) {   // chunks of hc heads, each chunk's key blocks heaviest first
+      const int per = hc * nkb, ch = s / per, r = s - ch * per;
+      kb = r / hc; bh = x + kXcdsB * (ch * hc + r % hc);
+    } else {
+      bh = x + kXcdsB * (s / nkb); kb = s % nkb;
+    }
   } else if (causal) {
     kb = id / BH; bh = id % BH;
   } else {
@@ -455,7 +463,7 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWK>), dim3(static_cast<unsigned>(static_cast<int64_t>(nkb) * BH)),
                      dim3(NWK * 64), 0, st, q, k, v, dout, a.lse, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, BH, nkb, c,
-                     a.scale, a.causal);
+                     a.scale, a.causal, causal_head_chunk(BH, 4LL * a.N * D));   // Q and dO bytes of a head
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -463,7 +471,8 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   const int nqb = (a.N + NWQ * 32 - 1) / (NWQ * 32);
   hipLaunchKernelGGL((bwd_dq_kernel<D, NWQ>), dim3(static_cast<unsigned>(static_cast<int64_t>(nqb) * BH)),
                      dim3(NWQ * 64), 0, st, q, k, v, dout, a.lse, a.delta,
-                     static_cast<uint16_t*>(a.dq), a.N, BH, nqb, c, a.scale, a.causal);
+                     static_cast<uint16_t*>(a.dq), a.N, BH, nqb, c, a.scale, a.causal,
+                     causal_head_chunk(BH, 4LL * a.N * D));   // K and V bytes of a head
   return hipGetLastError();
 }
 

@@ -154,7 +154,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
                 const uint8_t* __restrict__ v8, const void* __restrict__ sqv,
                 const void* __restrict__ skv, const void* __restrict__ svv,
                 uint16_t* __restrict__ o, float* __restrict__ lse, int N, int BH, int nqb,
-                int ntq, float c0) {
+                int ntq, float c0, int hc) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = Cfg8<D>;
   __shared__ __attribute__((aligned(1024))) char kring[2 * C::TILEB];     // fp8 K, two slots
@@ -173,9 +173,13 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   const int id = static_cast<int>(blockIdx.x);
   int bh, qbk;
   if (BH % kXcds8 == 0) {
-    const int x = id % kXcds8, s = id / kXcds8, hx = BH / kXcds8;
-    if (CAUSAL) { qbk = nqb - 1 - s / hx; bh = x + kXcds8 * (s % hx); }
-    else        { bh = x + kXcds8 * (s / nqb); qbk = s % nqb; }
+    const int x = id % kXcds8, s = id / kXcds8;
+    if (CAUSAL) {   // chunks of hc heads, each chunk's blocks heaviest first
+      const int per = hc * nqb, ch = s / per, r = s - ch * per;
+      qbk = nqb - 1 - r / hc; bh = x + kXcds8 * (ch * hc + r % hc);
+    } else {
+      bh = x + kXcds8 * (s / nqb); qbk = s % nqb;
+    }
   } else if (CAUSAL) {
     qbk = nqb - 1 - id / BH; bh = id % BH;
   } else {
@@ -413,9 +417,10 @@ hipError_t fwd_one(const Fp8Args& a) {
   const int nqb = (a.N + BR8 - 1) / BR8;
   const int ntq = (a.N + kTile8 - 1) / kTile8;
   const int64_t blocks = static_cast<int64_t>(nqb) * BH;
+  const int hc = causal_head_chunk(BH, 2LL * a.N * D);      // fp8 K and V bytes of a head
   hipLaunchKernelGGL((attn_fp8_kernel<D, CAUSAL, MX>), dim3(static_cast<unsigned>(blocks)), dim3(NT8), 0,
                      static_cast<hipStream_t>(a.stream), a.q8, a.k8, a.v8, a.sq, a.sk, a.sv,
-                     static_cast<uint16_t*>(a.o), a.lse, a.N, BH, nqb, ntq, a.scale * kLog2e);
+                     static_cast<uint16_t*>(a.o), a.lse, a.N, BH, nqb, ntq, a.scale * kLog2e, hc);
   return hipGetLastError();
 }
 

@@ -415,29 +415,13 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Causal launches walk an XCD's heads in chunks whose K and V total about
-// 16 MB (8 heads at N = 4096, d = 128; 2 at N = 16384), so that the query
-// blocks running side by side on an XCD read the same keys from its L2 and
-// the last-level cache instead of every CU streaming a different head from
-// HBM (measured: 1.30 -> 1.14 ms on B=8 H=32 N=4096, 2.24 -> 2.08 ms on
-// B=4 H=32 N=8192).  The chunk divides the XCD's share of heads.
-inline int causal_head_chunk(int BH, int N, int d) {
-  const int hx = BH % kXcds == 0 ? BH / kXcds : 1;
-  const int64_t kv = 4LL * N * d;                       // K and V bytes of one head
-  int64_t hc = (16LL << 20) / (kv > 0 ? kv : 1);
-  hc = hc < 1 ? 1 : (hc > hx ? hx : hc);
-  int h = static_cast<int>(hc);
-  while (hx % h) --h;
-  return h;
-}
-
 template <int D, int NW>
 hipError_t launch_one(const LaunchArgs& a) {
   using C = Cfg<D, NW>;
   const int BH = a.B * a.H;
   const int nqb = (a.N + C::BR - 1) / C::BR;
   const int64_t blocks = static_cast<int64_t>(nqb) * BH;
-  const int hc = causal_head_chunk(BH, a.N, D);
+  const int hc = causal_head_chunk(BH, 4LL * a.N * D);      // K and V bytes of a head
   hipLaunchKernelGGL((attn_mfma_bf16_kernel<D, NW>), dim3(static_cast<unsigned>(blocks)),
                      dim3(C::NT), 0, static_cast<hipStream_t>(a.stream),
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),

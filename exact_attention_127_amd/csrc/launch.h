@@ -9,6 +9,22 @@ namespace attn127 {
 // shared by the prepare and the forward kernels.
 constexpr int kFp8Tile = 128;
 
+// Causal launches walk an XCD's share of heads (the dispatcher sends
+// workgroup i to XCD i mod 8) in chunks whose per-head streamed bytes total
+// about 16 MB, so that the blocks running side by side on an XCD read the
+// same keys (or queries) from its L2 and the last-level cache instead of
+// every CU streaming a different head from HBM.  Measured on the bf16
+// forward: 1.30 -> 1.14 ms at B=8 H=32 N=4096, 2.24 -> 2.08 ms at B=4 H=32
+// N=8192.  The chunk divides the XCD's share of heads.
+inline int causal_head_chunk(int BH, int64_t head_bytes) {
+  const int hx = BH % 8 == 0 ? BH / 8 : 1;
+  int64_t hc = (int64_t(16) << 20) / (head_bytes > 0 ? head_bytes : 1);
+  hc = hc < 1 ? 1 : (hc > hx ? hx : hc);
+  int h = static_cast<int>(hc);
+  while (hx % h) --h;
+  return h;
+}
+
 struct LaunchArgs {
   const void* q;
   const void* k;
