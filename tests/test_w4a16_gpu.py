@@ -80,6 +80,16 @@ def test_gemm_long_rows(gpu, M, N, K):
     assert np.all(err <= bound), (float((err / bound).max()), M, N, K)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (16, 1, 256), (2, 3, 128), (16, 17, 128), (9, 5, 512)])
+def test_gemm_tiny_outputs(gpu, M, N, K):
+    # fewer output rows than one 16-row tile, N not a multiple of 4 (element stores)
+    inp = _case(M, N, K, 5 * M + N + K)
+    y = _gemm(inp, gpu)
+    err, bound, ref = _gate(y, inp)
+    assert y.shape == (M, N)
+    assert np.all(err <= bound), (float((err / bound).max()), M, N, K)
+
+
 def test_one_hot_selects_a_weight_column(gpu):
     inp = _case(4, 40, 512, 3)
     K = 512
