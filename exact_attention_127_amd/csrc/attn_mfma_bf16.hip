@@ -81,8 +81,6 @@ __device__ __forceinline__ int kswz(int row) { return D == 128 ? (row & 15) : ((
 template <int D>
 __device__ __forceinline__ int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
-// Scheduling-group masks (LLVM AMDGPU sched_group_barrier).
-constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100, kSgTrans = 0x400;
 
 // Device-only helpers (gfx950 builtins have no host-side meaning).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -138,32 +136,62 @@ struct LaneAddr {
   }
 };
 
+// MFMA counts per tile: both products take (BC/32)*(D/16) = (D/32)*(BC/16)
+// instructions, and each lane holds BC/4 pairs of scores (two keys of one
+// query), so every MFMA slot of a phase carries PPS pairs of vector work.
+template <int D>
+struct Ops {
+  static constexpr int NM = (BC / 32) * (D / 16);
+  static constexpr int PAIRS = BC / 4;
+  static constexpr int PPS = PAIRS / NM;
+  static_assert(NM == (D / 32) * (BC / 16) && PPS * NM == PAIRS, "phase shapes");
+};
+
+// A operand of score MFMA i (key block i / (D/16), channel step i % (D/16)).
+template <int D>
+__device__ __forceinline__ bf16x8 k_operand(const char* kst, const LaneAddr<D>& la, int i) {
+  const int kb = i / (D / 16), ks = i % (D / 16);
+  return *reinterpret_cast<const bf16x8*>(kst + kb * 32 * (2 * D) + la.kofs[ks]);
+}
+
+// A operand (V^T) of output MFMA i (channel block i / (BC/16), key step i % (BC/16)).
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(const char* vst, const LaneAddr<D>& la, int i) {
+  const int db = i / (BC / 16), c16 = i % (BC / 16);
+  const v4i16 lo = ds_read_tr16(vst + la.vbase[db] + (c16 * 16) * (2 * D));
+  const v4i16 hi = ds_read_tr16(vst + la.vbase[db] + (c16 * 16 + 8) * (2 * D));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // S^T = K Q^T for one tile (two 32-key blocks), K from LDS.
 template <int D>
 __device__ __forceinline__ void scores(f32x16 (&sacc)[BC / 32], const WaveState<D>& w,
-                                       const LaneAddr<D>& la, const char* kst, int h) {
+                                       const LaneAddr<D>& la, const char* kst) {
 #pragma unroll
-  for (int kb = 0; kb < BC / 32; ++kb) {
-    sacc[kb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * (2 * D) + la.kofs[ks]);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qr[ks], sacc[kb], 0, 0, 0);
-    }
+  for (int i = 0; i < Ops<D>::NM; ++i) {
+    const int kb = i / (D / 16), ks = i % (D / 16);
+    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<D>(kst, la, i), w.qr[ks],
+                                                       ks == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
   }
+}
+
+// Accumulator register r of key block kb holds key kv0 + 4h + key_off(kb, r)
+// (a compile-time offset below BC).  A key is visible when it is below N and,
+// causal, not past the query row, i.e. when key_off <= key_limit.
+__device__ __forceinline__ constexpr int key_off(int kb, int r) { return kb * 32 + 8 * (r >> 2) + (r & 3); }
+__device__ __forceinline__ int key_limit(int kv0, int N, int qrow, int h, bool causal) {
+  const int base = kv0 + 4 * h;
+  return causal ? min(N - 1, qrow) - base : N - 1 - base;
 }
 
 // Keys past the diagonal (causal) or past the sequence end -> -inf.
 __device__ __forceinline__ void apply_mask(f32x16 (&sacc)[BC / 32], int kv0, int N, int qrow, int h,
                                            bool causal) {
+  const int lim = key_limit(kv0, N, qrow, h, causal);
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      const bool masked = (key >= N) || (causal && key > qrow);
-      sacc[kb][r] = masked ? -INFINITY : sacc[kb][r];
-    }
+    for (int r = 0; r < 16; ++r) sacc[kb][r] = key_off(kb, r) > lim ? -INFINITY : sacc[kb][r];
 }
 
 __device__ __forceinline__ float tile_max(const f32x16 (&sacc)[BC / 32]) {
@@ -175,44 +203,68 @@ __device__ __forceinline__ float tile_max(const f32x16 (&sacc)[BC / 32]) {
   return mx;
 }
 
-// Raise the exponent reference if some row's tile maximum (already scaled
-// by c, both lane halves combined) exceeds it by more than kTau.
+// First tile: the exponent reference becomes the row's scaled maximum, and
+// the scores become exponents t = s*c - m in place.
 template <int D>
-__device__ __forceinline__ void update_reference(WaveState<D>& w, float mt) {
-  if (__builtin_amdgcn_ballot_w64(mt > w.m + kTau) != 0) {
-    const float mnew = fmaxf(w.m, mt);
-    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(w.m - mnew);
-    w.lsum *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
-    w.m = mnew;
-  }
-}
-
-// p = exp2(s*c - m) for one tile: the float32 p go into the normaliser, the
-// bf16-rounded p into the B operand of P V (16 keys per entry, in the
-// accumulator's key order).
-template <int D>
-__device__ __forceinline__ void softmax_tile(WaveState<D>& w, bf16x8 (&pb)[BC / 16],
-                                             const f32x16 (&sacc)[BC / 32], float c) {
+__device__ __forceinline__ void first_reference(WaveState<D>& w, f32x16 (&s)[BC / 32], float c) {
+  w.m = halves_max(tile_max(s)) * c;
   const float mref = (w.m == -INFINITY) ? 0.f : w.m;
-  uint32_t pw[BC / 16][4];
-  float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(fmaf(sacc[kb][r], c, -mref));
-      const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], c, -mref));
-      ls0 += p0;
-      ls1 += p1;
-      // accumulator registers 8c'..8c'+7 of block kb form operand 2kb+c'
-      pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-    }
-  w.lsum += ls0 + ls1;
+    for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -mref);
+}
+
+// Later tiles arrive as exponents against the current reference; mt is the
+// row's tile maximum of them (both lane halves).  The reference moves only
+// when some row exceeds it by more than kTau: then the normaliser and the
+// partial output are rescaled and the tile's exponents shifted to match.
+template <int D>
+__device__ __forceinline__ void shift_reference(WaveState<D>& w, f32x16 (&t)[BC / 32], float mt) {
+  if (__builtin_amdgcn_ballot_w64(mt > kTau) != 0) {
+    const float delta = fmaxf(mt, 0.f);        // rows with no visible key (-inf) keep theirs
+    const float alpha = fast_exp2(-delta);
+    w.lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
+    w.m += delta;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[kb][r] -= delta;
+  }
+}
+
+// p = exp2(t) for pair pr of a tile: the float32 p go into the normaliser,
+// the bf16-rounded p into the B operand of P V (accumulator registers
+// 8c'..8c'+7 of key block kb form operand 2kb+c').
+__device__ __forceinline__ void exp_pair(uint32_t (&pw)[BC / 16][4], float& ls0, float& ls1,
+                                         const f32x16 (&t)[BC / 32], int pr) {
+  const int kb = pr / 8, r = (pr % 8) * 2;
+  const float p0 = fast_exp2(t[kb][r]);
+  const float p1 = fast_exp2(t[kb][r + 1]);
+  ls0 += p0;
+  ls1 += p1;
+  pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+}
+
+template <int D>
+__device__ __forceinline__ void pack_operands(bf16x8 (&pb)[BC / 16], const uint32_t (&pw)[BC / 16][4]) {
 #pragma unroll
   for (int c16 = 0; c16 < BC / 16; ++c16)
     pb[c16] = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
+}
+
+// Softmax numerators of the last tile (not pipelined).
+template <int D>
+__device__ __forceinline__ void softmax_tile(WaveState<D>& w, bf16x8 (&pb)[BC / 16],
+                                             const f32x16 (&t)[BC / 32]) {
+  uint32_t pw[BC / 16][4];
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int pr = 0; pr < Ops<D>::PAIRS; ++pr) exp_pair(pw, ls0, ls1, t, pr);
+  w.lsum += ls0 + ls1;
+  pack_operands<D>(pb, pw);
 }
 
 // O^T += V^T P^T for one tile, V^T through transposing LDS reads.
@@ -220,57 +272,91 @@ template <int D>
 __device__ __forceinline__ void pv_tile(WaveState<D>& w, const bf16x8 (&pb)[BC / 16],
                                         const LaneAddr<D>& la, const char* vst) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int c16 = 0; c16 < BC / 16; ++c16) {
-      const v4i16 lo = ds_read_tr16(vst + la.vbase[db] + (c16 * 16) * (2 * D));
-      const v4i16 hi = ds_read_tr16(vst + la.vbase[db] + (c16 * 16 + 8) * (2 * D));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c16], w.oacc[db], 0, 0, 0);
-    }
+  for (int i = 0; i < Ops<D>::NM; ++i) {
+    const int db = i / (BC / 16), c16 = i % (BC / 16);
+    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vst, la, i), pb[c16], w.oacc[db], 0, 0, 0);
+  }
 }
 
-// Phase A of a pipelined tile: scores of the next tile on the matrix cores,
-// interleaved with the exponentials of the current tile on the vector ALUs.
+// An empty volatile use: the value must be computed before this point, so
+// code sinking cannot move a slot's vector work out of its slot (the
+// scheduling barriers only act after instruction selection).
+template <typename T>
+__device__ __forceinline__ void pin(T x) { asm volatile("" ::"v"(x)); }
+
+// The two phases of a pipelined tile are written slot by slot: slot i holds
+// MFMA i, the LDS read of the operand a few MFMAs ahead, and PPS pairs of
+// the tile's vector work, and a scheduling barrier closes every slot, so the
+// matrix and vector pipes are fed side by side in one wave instead of as two
+// blocks (measured on an instruction-level model of the tile: 1474 ns as
+// blocks, 1125 ns slotted and balanced).
+constexpr int kReadAheadK = 3;   // score operands in flight
+constexpr int kReadAheadV = 2;   // output operands in flight (two reads each)
+
+// Phase A: scores of the next tile on the matrix cores beside the
+// exponentials, normaliser and bf16 packing of the current tile.
 template <int D>
 __device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32],
-                                        bf16x8 (&pb)[BC / 16], const f32x16 (&scur)[BC / 32],
-                                        const LaneAddr<D>& la, const char* kst_next, int h,
-                                        float c) {
+                                        bf16x8 (&pb)[BC / 16], const f32x16 (&tcur)[BC / 32],
+                                        const LaneAddr<D>& la, const char* kst_next) {
+  constexpr int NM = Ops<D>::NM, PPS = Ops<D>::PPS, KA = kReadAheadK;
+  bf16x8 kop[NM];
+  uint32_t pw[BC / 16][4];
+  float ls0 = 0.f, ls1 = 0.f;
   __builtin_amdgcn_sched_barrier(0);
-  scores<D>(snext, w, la, kst_next, h);
-  softmax_tile<D>(w, pb, scur, c);
-  constexpr int nm = (BC / 32) * (D / 16);     // MFMAs in the block
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
 #pragma unroll
-  for (int i = 0; i < nm; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    if (i + 4 < nm) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgTrans, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, 5, 0);
+  for (int i = 0; i < KA; ++i) kop[i] = k_operand<D>(kst_next, la, i);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i + KA < NM) kop[i + KA] = k_operand<D>(kst_next, la, i + KA);
+    const int kb = i / (D / 16), ks = i % (D / 16);
+    snext[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], w.qr[ks],
+                                                        ks == 0 ? f32x16{} : snext[kb], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < PPS; ++u) {
+      const int pr = i * PPS + u, kb2 = pr / 8, r = (pr % 8) * 2;
+      exp_pair(pw, ls0, ls1, tcur, pr);
+      pin(pw[kb2 * 2 + (r >> 3)][(r & 7) >> 1]);
+    }
+    pin(ls0);
+    pin(ls1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
+  w.lsum += ls0 + ls1;
+  pack_operands<D>(pb, pw);
 }
 
-// Phase B: P V of the current tile on the matrix cores, interleaved with the
-// (masked) row maximum of the next tile on the vector ALUs.
-template <int D, bool MASK>
+// Phase B: P V of the current tile on the matrix cores beside the scaling
+// (t = s*c - m) and row maximum of the next tile, whose masked keys (causal
+// diagonal, sequence end) were set to -inf before the phase.
+template <int D>
 __device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32],
                                          const bf16x8 (&pb)[BC / 16], const LaneAddr<D>& la,
-                                         const char* vst, int kv0n, int N, int qrow, int h, bool causal) {
+                                         const char* vst, float c) {
+  constexpr int NM = Ops<D>::NM, PPS = Ops<D>::PPS, VA = kReadAheadV;
+  bf16x8 vop[NM];
+  const float mref = w.m;
+  float mx = -INFINITY;
   __builtin_amdgcn_sched_barrier(0);
-  pv_tile<D>(w, pb, la, vst);
-  if (MASK) apply_mask(snext, kv0n, N, qrow, h, causal);
-  const float mx = tile_max(snext);
-  constexpr int nm = (D / 32) * (BC / 16);
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
 #pragma unroll
-  for (int i = 0; i < nm; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    if (i + 2 < nm) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, MASK ? 6 : 2, 0);
+  for (int i = 0; i < VA; ++i) vop[i] = v_operand<D>(vst, la, i);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i + VA < NM) vop[i + VA] = v_operand<D>(vst, la, i + VA);
+    const int db = i / (BC / 16), c16 = i % (BC / 16);
+    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], pb[c16], w.oacc[db], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < PPS; ++u) {
+      const int pr = i * PPS + u, kb = pr / 8, r = (pr % 8) * 2;
+      snext[kb][r] = fmaf(snext[kb][r], c, -mref);           // -inf stays -inf (c > 0)
+      snext[kb][r + 1] = fmaf(snext[kb][r + 1], c, -mref);
+      mx = fmaxf(mx, fmaxf(snext[kb][r], snext[kb][r + 1]));
+      pin(snext[kb][r]);
+      pin(snext[kb][r + 1]);
+    }
+    pin(mx);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
   return mx;
 }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -358,9 +444,9 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   f32x16 sa[BC / 32], sb[BC / 32];   // scores of the current and the next tile
   bf16x8 pb[BC / 16];
   if (last >= 0) {
-    scores<D>(sa, w, la, kring, h);
+    scores<D>(sa, w, la, kring);
     if ((causal && BC - 1 > q0w) || BC > N) apply_mask(sa, 0, N, qrow, h, causal);
-    update_reference<D>(w, halves_max(tile_max(sa)) * c);
+    first_reference<D>(w, sa, c);
   }
   __syncthreads();   // every wave is done with K0 before its slot is refilled
 
@@ -376,14 +462,13 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (t + 2 < ntiles) issue_copy<D, NW, false>(kring + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
     if (t < last) {
       const int kv0n = (t + 1) * BC;
-      phase_a<D>(w, snext, pb, scur, la, kst_next, h, c);
+      phase_a<D>(w, snext, pb, scur, la, kst_next);
       const bool mask_next = (causal && kv0n + BC - 1 > q0w) || (kv0n + BC > N);
-      float mx;
-      if (mask_next) mx = phase_b<D, true>(w, snext, pb, la, vst, kv0n, N, qrow, h, causal);
-      else           mx = phase_b<D, false>(w, snext, pb, la, vst, kv0n, N, qrow, h, causal);
-      update_reference<D>(w, halves_max(mx) * c);
+      if (mask_next) apply_mask(snext, kv0n, N, qrow, h, causal);
+      const float mx = phase_b<D>(w, snext, pb, la, vst, c);
+      shift_reference<D>(w, snext, halves_max(mx));
     } else if (t == last) {
-      softmax_tile<D>(w, pb, scur, c);
+      softmax_tile<D>(w, pb, scur);
       pv_tile<D>(w, pb, la, vst);
     }
     wait_vmcnt<0>();
