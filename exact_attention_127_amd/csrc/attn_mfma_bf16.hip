@@ -203,38 +203,6 @@ __device__ __forceinline__ float tile_max(const f32x16 (&sacc)[BC / 32]) {
   return mx;
 }
 
-// First tile: the exponent reference becomes the row's scaled maximum, and
-// the scores become exponents t = s*c - m in place.
-template <int D>
-__device__ __forceinline__ void first_reference(WaveState<D>& w, f32x16 (&s)[BC / 32], float c) {
-  w.m = halves_max(tile_max(s)) * c;
-  const float mref = (w.m == -INFINITY) ? 0.f : w.m;
-#pragma unroll
-  for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -mref);
-}
-
-// Later tiles arrive as exponents against the current reference; mt is the
-// row's tile maximum of them (both lane halves).  The reference moves only
-// when some row exceeds it by more than kTau: then the normaliser and the
-// partial output are rescaled and the tile's exponents shifted to match.
-template <int D>
-__device__ __forceinline__ void shift_reference(WaveState<D>& w, f32x16 (&t)[BC / 32], float mt) {
-  if (__builtin_amdgcn_ballot_w64(mt > kTau) != 0) {
-    const float delta = fmaxf(mt, 0.f);        // rows with no visible key (-inf) keep theirs
-    const float alpha = fast_exp2(-delta);
-    w.lsum *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
-    w.m += delta;
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) t[kb][r] -= delta;
-  }
-}
-
 // p = exp2(t) for pair pr of a tile: the float32 p go into the normaliser,
 // the bf16-rounded p into the B operand of P V (accumulator registers
 // 8c'..8c'+7 of key block kb form operand 2kb+c').
@@ -248,33 +216,108 @@ __device__ __forceinline__ void exp_pair(uint32_t (&pw)[BC / 16][4], float& ls0,
   pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
 }
 
-template <int D>
-__device__ __forceinline__ void pack_operands(bf16x8 (&pb)[BC / 16], const uint32_t (&pw)[BC / 16][4]) {
+// The last P operand of a tile (its last 16 keys: score pairs kFirstEarly..
+// of the second key block) is formed one phase early, in the P V phase of
+// the previous tile, right after that tile's exponents are known; the rest
+// follows in the score phase.  This moves a quarter of the exponential work
+// to the phase whose vector pipe is otherwise half idle (measured on an
+// instruction-level model of the tile: 1096 -> 1022 ns).
+constexpr int kEarly = 4;                       // pairs formed early
+constexpr int kFirstEarly = BC / 4 - kEarly;    // = 12
+constexpr int kLateOps = BC / 16 - 1;           // P operands formed in the score phase
+static_assert(kEarly * 4 == 16 && kFirstEarly % 8 == 4, "early pairs fill the last operand");
+
+__device__ __forceinline__ void exp_early(uint32_t (&pw)[4], float& l0, float& l1,
+                                          const f32x16 (&t)[BC / 32], int k) {
+  const int r = ((kFirstEarly + k) % 8) * 2;     // key block BC/32 - 1
+  const float p0 = fast_exp2(t[BC / 32 - 1][r]);
+  const float p1 = fast_exp2(t[BC / 32 - 1][r + 1]);
+  l0 += p0;
+  l1 += p1;
+  pw[k] = pack_bf16x2(p0, p1);
+}
+
+// All early pairs of a tile at once (first tile, and after a reference shift).
+__device__ __forceinline__ void early_operand(bf16x8& pe, float& le, const f32x16 (&t)[BC / 32]) {
+  uint32_t pw[4];
+  float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-  for (int c16 = 0; c16 < BC / 16; ++c16)
+  for (int k = 0; k < kEarly; ++k) exp_early(pw, l0, l1, t, k);
+  pe = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+  le = l0 + l1;
+}
+
+// First tile: the exponent reference becomes the row's scaled maximum, the
+// scores become exponents t = s*c - m in place, and the early operand forms.
+template <int D>
+__device__ __forceinline__ void first_reference(WaveState<D>& w, f32x16 (&s)[BC / 32], float c,
+                                                bf16x8& pe, float& le) {
+  w.m = halves_max(tile_max(s)) * c;
+  const float mref = (w.m == -INFINITY) ? 0.f : w.m;
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -mref);
+  early_operand(pe, le, s);
+}
+
+// Later tiles arrive as exponents against the current reference; mt is the
+// row's tile maximum of them (both lane halves).  The reference moves only
+// when some row exceeds it by more than kTau: then the normaliser and the
+// partial output are rescaled, the tile's exponents shifted to match and its
+// early operand formed again.
+template <int D>
+__device__ __forceinline__ void shift_reference(WaveState<D>& w, f32x16 (&t)[BC / 32], float mt,
+                                                bf16x8& pe, float& le) {
+  if (__builtin_amdgcn_ballot_w64(mt > kTau) != 0) {
+    const float delta = fmaxf(mt, 0.f);        // rows with no visible key (-inf) keep theirs
+    const float alpha = fast_exp2(-delta);
+    w.lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
+    w.m += delta;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[kb][r] -= delta;
+    early_operand(pe, le, t);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pack_operands(bf16x8 (&pb)[kLateOps], const uint32_t (&pw)[BC / 16][4]) {
+#pragma unroll
+  for (int c16 = 0; c16 < kLateOps; ++c16)
     pb[c16] = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
 }
 
-// Softmax numerators of the last tile (not pipelined).
+// Softmax numerators of the last tile (not pipelined; the early operand and
+// its sum are already there).
 template <int D>
-__device__ __forceinline__ void softmax_tile(WaveState<D>& w, bf16x8 (&pb)[BC / 16],
-                                             const f32x16 (&t)[BC / 32]) {
+__device__ __forceinline__ void softmax_tile(WaveState<D>& w, bf16x8 (&pb)[kLateOps],
+                                             const f32x16 (&t)[BC / 32], float le) {
   uint32_t pw[BC / 16][4];
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-  for (int pr = 0; pr < Ops<D>::PAIRS; ++pr) exp_pair(pw, ls0, ls1, t, pr);
-  w.lsum += ls0 + ls1;
+  for (int pr = 0; pr < kFirstEarly; ++pr) exp_pair(pw, ls0, ls1, t, pr);
+  w.lsum += (ls0 + ls1) + le;
   pack_operands<D>(pb, pw);
+}
+
+template <int D>
+__device__ __forceinline__ const bf16x8& p_operand(const bf16x8 (&pb)[kLateOps], const bf16x8& pe, int c16) {
+  return c16 < kLateOps ? pb[c16] : pe;
 }
 
 // O^T += V^T P^T for one tile, V^T through transposing LDS reads.
 template <int D>
-__device__ __forceinline__ void pv_tile(WaveState<D>& w, const bf16x8 (&pb)[BC / 16],
+__device__ __forceinline__ void pv_tile(WaveState<D>& w, const bf16x8 (&pb)[kLateOps], const bf16x8& pe,
                                         const LaneAddr<D>& la, const char* vst) {
 #pragma unroll
   for (int i = 0; i < Ops<D>::NM; ++i) {
     const int db = i / (BC / 16), c16 = i % (BC / 16);
-    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vst, la, i), pb[c16], w.oacc[db], 0, 0, 0);
+    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vst, la, i), p_operand<D>(pb, pe, c16),
+                                                         w.oacc[db], 0, 0, 0);
   }
 }
 
@@ -285,21 +328,22 @@ template <typename T>
 __device__ __forceinline__ void pin(T x) { asm volatile("" ::"v"(x)); }
 
 // The two phases of a pipelined tile are written slot by slot: slot i holds
-// MFMA i, the LDS read of the operand a few MFMAs ahead, and PPS pairs of
-// the tile's vector work, and a scheduling barrier closes every slot, so the
-// matrix and vector pipes are fed side by side in one wave instead of as two
-// blocks (measured on an instruction-level model of the tile: 1474 ns as
-// blocks, 1125 ns slotted and balanced).
+// MFMA i, the LDS read of the operand a few MFMAs ahead, and a share of the
+// vector work, and a scheduling barrier closes every slot, so the matrix and
+// vector pipes are fed side by side in one wave instead of as two blocks
+// (measured on an instruction-level model of the tile: 1474 ns as blocks,
+// 1096 ns slotted).
 constexpr int kReadAheadK = 3;   // score operands in flight
 constexpr int kReadAheadV = 2;   // output operands in flight (two reads each)
 
 // Phase A: scores of the next tile on the matrix cores beside the
-// exponentials, normaliser and bf16 packing of the current tile.
+// exponentials, normaliser and bf16 packing of the current tile's first
+// kFirstEarly pairs (spread evenly over the slots).
 template <int D>
 __device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32],
-                                        bf16x8 (&pb)[BC / 16], const f32x16 (&tcur)[BC / 32],
-                                        const LaneAddr<D>& la, const char* kst_next) {
-  constexpr int NM = Ops<D>::NM, PPS = Ops<D>::PPS, KA = kReadAheadK;
+                                        bf16x8 (&pb)[kLateOps], const f32x16 (&tcur)[BC / 32],
+                                        float lecur, const LaneAddr<D>& la, const char* kst_next) {
+  constexpr int NM = Ops<D>::NM, KA = kReadAheadK;
   bf16x8 kop[NM];
   uint32_t pw[BC / 16][4];
   float ls0 = 0.f, ls1 = 0.f;
@@ -313,8 +357,9 @@ __device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32
     snext[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], w.qr[ks],
                                                         ks == 0 ? f32x16{} : snext[kb], 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < PPS; ++u) {
-      const int pr = i * PPS + u, kb2 = pr / 8, r = (pr % 8) * 2;
+    for (int pr = 0; pr < kFirstEarly; ++pr) {
+      if ((pr * NM) / kFirstEarly != i) continue;
+      const int kb2 = pr / 8, r = (pr % 8) * 2;
       exp_pair(pw, ls0, ls1, tcur, pr);
       pin(pw[kb2 * 2 + (r >> 3)][(r & 7) >> 1]);
     }
@@ -322,19 +367,24 @@ __device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32
     pin(ls1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  w.lsum += ls0 + ls1;
+  w.lsum += (ls0 + ls1) + lecur;
   pack_operands<D>(pb, pw);
 }
 
 // Phase B: P V of the current tile on the matrix cores beside the scaling
 // (t = s*c - m) and row maximum of the next tile, whose masked keys (causal
-// diagonal, sequence end) were set to -inf before the phase.
+// diagonal, sequence end) were set to -inf before the phase, and the next
+// tile's early operand.  The early pairs are scaled first.
 template <int D>
 __device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32],
-                                         const bf16x8 (&pb)[BC / 16], const LaneAddr<D>& la,
+                                         const bf16x8 (&pb)[kLateOps], const bf16x8& pecur,
+                                         bf16x8& penext, float& lenext, const LaneAddr<D>& la,
                                          const char* vst, float c) {
   constexpr int NM = Ops<D>::NM, PPS = Ops<D>::PPS, VA = kReadAheadV;
+  constexpr int S0 = kEarly / PPS;               // slots that scale the early pairs
   bf16x8 vop[NM];
+  uint32_t pw[4];
+  float l0 = 0.f, l1 = 0.f;
   const float mref = w.m;
   float mx = -INFINITY;
   __builtin_amdgcn_sched_barrier(0);
@@ -344,19 +394,29 @@ __device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 3
   for (int i = 0; i < NM; ++i) {
     if (i + VA < NM) vop[i + VA] = v_operand<D>(vst, la, i + VA);
     const int db = i / (BC / 16), c16 = i % (BC / 16);
-    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], pb[c16], w.oacc[db], 0, 0, 0);
+    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], p_operand<D>(pb, pecur, c16), w.oacc[db], 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < PPS; ++u) {
-      const int pr = i * PPS + u, kb = pr / 8, r = (pr % 8) * 2;
+      const int pr = (i * PPS + u + kFirstEarly) % Ops<D>::PAIRS, kb = pr / 8, r = (pr % 8) * 2;
       snext[kb][r] = fmaf(snext[kb][r], c, -mref);           // -inf stays -inf (c > 0)
       snext[kb][r + 1] = fmaf(snext[kb][r + 1], c, -mref);
       mx = fmaxf(mx, fmaxf(snext[kb][r], snext[kb][r + 1]));
       pin(snext[kb][r]);
       pin(snext[kb][r + 1]);
     }
+#pragma unroll
+    for (int k = 0; k < kEarly; ++k) {
+      if (S0 + (k * (NM - S0)) / kEarly != i) continue;
+      exp_early(pw, l0, l1, snext, k);
+      pin(pw[k]);
+      pin(l0);
+      pin(l1);
+    }
     pin(mx);
     __builtin_amdgcn_sched_barrier(0);
   }
+  penext = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+  lenext = l0 + l1;
   return mx;
 }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -442,11 +502,13 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __syncthreads();
 
   f32x16 sa[BC / 32], sb[BC / 32];   // scores of the current and the next tile
-  bf16x8 pb[BC / 16];
+  bf16x8 pea, peb;                   // their early P operands ...
+  float lea = 0.f, leb = 0.f;        // ... and those operands' normaliser shares
+  bf16x8 pb[kLateOps];
   if (last >= 0) {
     scores<D>(sa, w, la, kring);
     if ((causal && BC - 1 > q0w) || BC > N) apply_mask(sa, 0, N, qrow, h, causal);
-    first_reference<D>(w, sa, c);
+    first_reference<D>(w, sa, c, pea, lea);
   }
   __syncthreads();   // every wave is done with K0 before its slot is refilled
 
@@ -455,28 +517,29 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // in LDS.  Iteration t copies V of t+1 and K of t+2.
   // The score buffers alternate roles each tile; two tiles per trip keep
   // that choice static.
-  auto iteration = [&](int t, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32]) {
+  auto iteration = [&](int t, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32], bf16x8& pecur,
+                       bf16x8& penext, float& lecur, float& lenext) {
     const char* kst_next = kring + ((t + 1) & 1) * C::TILEB;
     const char* vst = vring + (t & 1) * C::TILEB;
     if (t + 1 < ntiles) issue_copy<D, NW, true>(vring + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave, lane);
     if (t + 2 < ntiles) issue_copy<D, NW, false>(kring + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
     if (t < last) {
       const int kv0n = (t + 1) * BC;
-      phase_a<D>(w, snext, pb, scur, la, kst_next);
+      phase_a<D>(w, snext, pb, scur, lecur, la, kst_next);
       const bool mask_next = (causal && kv0n + BC - 1 > q0w) || (kv0n + BC > N);
       if (mask_next) apply_mask(snext, kv0n, N, qrow, h, causal);
-      const float mx = phase_b<D>(w, snext, pb, la, vst, c);
-      shift_reference<D>(w, snext, halves_max(mx));
+      const float mx = phase_b<D>(w, snext, pb, pecur, penext, lenext, la, vst, c);
+      shift_reference<D>(w, snext, halves_max(mx), penext, lenext);
     } else if (t == last) {
-      softmax_tile<D>(w, pb, scur);
-      pv_tile<D>(w, pb, la, vst);
+      softmax_tile<D>(w, pb, scur, lecur);
+      pv_tile<D>(w, pb, pecur, la, vst);
     }
     wait_vmcnt<0>();
     __syncthreads();
   };
   for (int t = 0; t < ntiles; t += 2) {
-    iteration(t, sa, sb);
-    if (t + 1 < ntiles) iteration(t + 1, sb, sa);
+    iteration(t, sa, sb, pea, peb, lea, leb);
+    if (t + 1 < ntiles) iteration(t + 1, sb, sa, peb, pea, leb, lea);
   }
 
   // ---- epilogue: the deferred division, bf16 output, LSE ----
