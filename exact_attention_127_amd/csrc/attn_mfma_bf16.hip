@@ -33,11 +33,12 @@
 //    and V of tile t+1 are copied while tile t is processed; one barrier per
 //    tile.  Out-of-range rows read as zero (buffer bounds).  16-byte chunks
 //    are XOR-swizzled per row so the operand reads hit distinct LDS banks.
-//  * The running maximum used as the exponent reference is only raised when
-//    some row's tile maximum exceeds it by more than kTau (base 2); p then
-//    stays <= 2^kTau, the normaliser and the partial output carry the same
-//    reference, and the single division at the end cancels it exactly.  Most
-//    tiles of a long row therefore skip the rescale of the partial output.
+//  * The exponent reference is the first tile's row maximum and moves only
+//    when a tile's numerators would grow past 2^16, detected from their sum
+//    (which the normaliser needs anyway) instead of a per-element maximum;
+//    the normaliser and the partial output carry the same reference, and the
+//    single division at the end cancels it exactly.  Most tiles of a long
+//    row therefore skip both the maximum and the rescale.
 //  * Two workgroups share a CU (one wave of each per SIMD), so one hides the
 //    other's barrier and copy waits.  Work items are grouped by XCD
 //    (dispatch is round-robin over the 8 XCDs) so the query blocks of one
@@ -53,7 +54,6 @@ namespace {
 
 constexpr int BRW = 32;          // query rows per wave
 constexpr int BC = 64;           // keys per tile
-constexpr float kTau = 8.0f;     // allowed growth of p above 1, as a power of two
 constexpr int kXcds = 8;
 
 // NW waves per workgroup: 8 (two per SIMD, sharing each K/V tile) or 4
@@ -261,27 +261,21 @@ __device__ __forceinline__ void first_reference(WaveState<D>& w, f32x16 (&s)[BC 
   early_operand(pe, le, s);
 }
 
-// Later tiles arrive as exponents against the current reference; mt is the
-// row's tile maximum of them (both lane halves).  The reference moves only
-// when some row exceeds it by more than kTau: then the normaliser and the
-// partial output are rescaled, the tile's exponents shifted to match and its
-// early operand formed again.
+// Later tiles arrive as exponents t = s*c - m against the current reference
+// m, which only moves when a tile would overflow it: the guard is the
+// per-lane sum of the tile's numerators (every p <= that sum), computed
+// anyway for the normaliser, so no per-element maximum is needed.  When a
+// lane's sum exceeds 2^kGuard (or is not finite), the tile's exact maximum
+// becomes the reference: the partial output and the normaliser of earlier
+// tiles are rescaled, the tile's exponents shifted, and its numerators
+// formed again.  p therefore stays below 2^kGuard, which float32 sums and
+// bf16 operands carry without loss of relative precision, and the final
+// division cancels the reference exactly.
+constexpr float kGuard = 65536.f;      // 2^16
+
 template <int D>
-__device__ __forceinline__ void shift_reference(WaveState<D>& w, f32x16 (&t)[BC / 32], float mt,
-                                                bf16x8& pe, float& le) {
-  if (__builtin_amdgcn_ballot_w64(mt > kTau) != 0) {
-    const float delta = fmaxf(mt, 0.f);        // rows with no visible key (-inf) keep theirs
-    const float alpha = fast_exp2(-delta);
-    w.lsum *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
-    w.m += delta;
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) t[kb][r] -= delta;
-    early_operand(pe, le, t);
-  }
+__device__ __forceinline__ bool tile_overflows(float lsum_tile) {
+  return __builtin_amdgcn_ballot_w64(!(lsum_tile <= kGuard)) != 0;
 }
 
 template <int D>
@@ -291,17 +285,43 @@ __device__ __forceinline__ void pack_operands(bf16x8 (&pb)[kLateOps], const uint
     pb[c16] = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
 }
 
-// Softmax numerators of the last tile (not pipelined; the early operand and
-// its sum are already there).
+// Numerators of a tile's late pairs at once (the last tile, which is not
+// pipelined, and the overflow path); ll receives their sum.
 template <int D>
-__device__ __forceinline__ void softmax_tile(WaveState<D>& w, bf16x8 (&pb)[kLateOps],
-                                             const f32x16 (&t)[BC / 32], float le) {
+__device__ __forceinline__ void late_operands(bf16x8 (&pb)[kLateOps], float& ll, const f32x16 (&t)[BC / 32]) {
   uint32_t pw[BC / 16][4];
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int pr = 0; pr < kFirstEarly; ++pr) exp_pair(pw, ls0, ls1, t, pr);
-  w.lsum += (ls0 + ls1) + le;
+  ll = ls0 + ls1;
   pack_operands<D>(pb, pw);
+}
+
+// Overflow path: the tile's exact maximum exponent becomes the reference
+// (rows whose maximum is not above it keep theirs).
+template <int D>
+__device__ __forceinline__ void rebase_tile(WaveState<D>& w, f32x16 (&t)[BC / 32], bf16x8 (&pb)[kLateOps],
+                                            bf16x8& pe, float& le, float& ll) {
+  const float delta = fmaxf(halves_max(tile_max(t)), 0.f);
+  const float alpha = fast_exp2(-delta);
+  w.lsum *= alpha;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
+  w.m += delta;
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[kb][r] -= delta;
+  early_operand(pe, le, t);
+  late_operands<D>(pb, ll, t);
+}
+
+// The guard and the normaliser update of a tile whose numerators are formed.
+template <int D>
+__device__ __forceinline__ void commit_tile(WaveState<D>& w, f32x16 (&t)[BC / 32], bf16x8 (&pb)[kLateOps],
+                                            bf16x8& pe, float& le, float ll) {
+  if (tile_overflows<D>(ll + le)) rebase_tile<D>(w, t, pb, pe, le, ll);
+  w.lsum += ll + le;
 }
 
 template <int D>
@@ -341,8 +361,8 @@ constexpr int kReadAheadV = 2;   // output operands in flight (two reads each)
 // kFirstEarly pairs (spread evenly over the slots).
 template <int D>
 __device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32],
-                                        bf16x8 (&pb)[kLateOps], const f32x16 (&tcur)[BC / 32],
-                                        float lecur, const LaneAddr<D>& la, const char* kst_next) {
+                                        bf16x8 (&pb)[kLateOps], float& ll, const f32x16 (&tcur)[BC / 32],
+                                        const LaneAddr<D>& la, const char* kst_next) {
   constexpr int NM = Ops<D>::NM, KA = kReadAheadK;
   bf16x8 kop[NM];
   uint32_t pw[BC / 16][4];
@@ -367,16 +387,16 @@ __device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32
     pin(ls1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  w.lsum += (ls0 + ls1) + lecur;
+  ll = ls0 + ls1;
   pack_operands<D>(pb, pw);
 }
 
 // Phase B: P V of the current tile on the matrix cores beside the scaling
-// (t = s*c - m) and row maximum of the next tile, whose masked keys (causal
-// diagonal, sequence end) were set to -inf before the phase, and the next
-// tile's early operand.  The early pairs are scaled first.
+// (t = s*c - m) of the next tile, whose masked keys (causal diagonal,
+// sequence end) were set to -inf before the phase, and the next tile's
+// early operand.  The early pairs are scaled first.
 template <int D>
-__device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32],
+__device__ __forceinline__ void phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32],
                                          const bf16x8 (&pb)[kLateOps], const bf16x8& pecur,
                                          bf16x8& penext, float& lenext, const LaneAddr<D>& la,
                                          const char* vst, float c) {
@@ -386,7 +406,6 @@ __device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 3
   uint32_t pw[4];
   float l0 = 0.f, l1 = 0.f;
   const float mref = w.m;
-  float mx = -INFINITY;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < VA; ++i) vop[i] = v_operand<D>(vst, la, i);
@@ -400,7 +419,6 @@ __device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 3
       const int pr = (i * PPS + u + kFirstEarly) % Ops<D>::PAIRS, kb = pr / 8, r = (pr % 8) * 2;
       snext[kb][r] = fmaf(snext[kb][r], c, -mref);           // -inf stays -inf (c > 0)
       snext[kb][r + 1] = fmaf(snext[kb][r + 1], c, -mref);
-      mx = fmaxf(mx, fmaxf(snext[kb][r], snext[kb][r + 1]));
       pin(snext[kb][r]);
       pin(snext[kb][r + 1]);
     }
@@ -412,12 +430,10 @@ __device__ __forceinline__ float phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 3
       pin(l0);
       pin(l1);
     }
-    pin(mx);
     __builtin_amdgcn_sched_barrier(0);
   }
   penext = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
   lenext = l0 + l1;
-  return mx;
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
@@ -525,13 +541,16 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (t + 2 < ntiles) issue_copy<D, NW, false>(kring + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
     if (t < last) {
       const int kv0n = (t + 1) * BC;
-      phase_a<D>(w, snext, pb, scur, lecur, la, kst_next);
+      float ll;
+      phase_a<D>(w, snext, pb, ll, scur, la, kst_next);
+      commit_tile<D>(w, scur, pb, pecur, lecur, ll);
       const bool mask_next = (causal && kv0n + BC - 1 > q0w) || (kv0n + BC > N);
       if (mask_next) apply_mask(snext, kv0n, N, qrow, h, causal);
-      const float mx = phase_b<D>(w, snext, pb, pecur, penext, lenext, la, vst, c);
-      shift_reference<D>(w, snext, halves_max(mx), penext, lenext);
+      phase_b<D>(w, snext, pb, pecur, penext, lenext, la, vst, c);
     } else if (t == last) {
-      softmax_tile<D>(w, pb, scur, lecur);
+      float ll;
+      late_operands<D>(pb, ll, scur);
+      commit_tile<D>(w, scur, pb, pecur, lecur, ll);
       pv_tile<D>(w, pb, pecur, la, vst);
     }
     wait_vmcnt<0>();

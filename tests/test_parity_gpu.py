@@ -11,7 +11,7 @@ import pytest
 
 import exact_attention_127_amd as A
 import oracle
-from seeded_inputs import WORKLOADS, make_inputs, random_inputs
+from seeded_inputs import WORKLOADS, make_inputs, random_inputs, round_to_bf16_bits
 from tests.helpers import err_stats, oracle_rows, sample_rows, to_device
 
 pytestmark = pytest.mark.gpu
@@ -118,6 +118,35 @@ def test_llm_layer_4k(gpu):
     """B=8 H=32 N=4096 d=128 causal, per-head Q/K factor: |O| can exceed 4,
     where bf16 output rounding alone passes 1e-2, so the excess is gated."""
     _check_sampled("llm_layer_4k", gpu, 10, excess_gate=True)
+
+
+def _rising_inputs(N, d, causal, rise, seed):
+    """Scores that grow along the keys by ``rise`` (natural-log units) per 64
+    keys: q_i ~ sqrt(d) g and k_j ~ (rise j / 64) g for a unit vector g, plus
+    small noise, so scale * q_i . k_j ~ rise j / 64."""
+    rng = np.random.default_rng(seed)
+    B, H = 1, 2
+    g = rng.standard_normal(d)
+    g /= np.linalg.norm(g)
+    ramp = rise * np.arange(N) / 64.0
+    q = np.sqrt(d) * g + 0.05 * rng.standard_normal((B, H, N, d))
+    k = ramp[:, None] * g + 0.05 * rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    q, k, v = (round_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+    return {"q": q, "k": k, "v": v, "scale": float(d) ** -0.5, "causal": causal}
+
+
+@pytest.mark.parametrize("rise", [3.0, 20.0, 100.0])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_move_the_reference(gpu, rise, d, causal):
+    """Each key tile's numerators outgrow the exponent reference that earlier
+    tiles set: at 3 per 64 keys the reference moves every few tiles, at 20
+    every tile, and at 100 (144 in base 2) the numerators against the old
+    reference would not even be finite in float32.  The kernel's overflow
+    path must take the tile's own maximum as the new reference each time."""
+    inp = _rising_inputs(300, d, causal, rise, seed=int(rise) * 10 + d + causal)
+    _check_full(A.attn_fwd, inp, gpu, "bf16", small=True)
 
 
 def test_causal_row0_equals_v0(gpu):
