@@ -86,8 +86,9 @@ __device__ __forceinline__ int vswz(int row) { return D == 128 ? ((row & 3) << 2
 #if defined(__HIP_DEVICE_COMPILE__)
 // Copy rows [kv0, kv0+BC) of one (b,h) slice of K or V into an LDS tile;
 // each wave copies BPW one-kilobyte blocks.
+// dst: the tile's LDS byte address (wave-uniform).
 template <int D, int NW, bool IS_V>
-__device__ __forceinline__ void issue_copy(char* dst, const uint16_t* src, int kv0, int N,
+__device__ __forceinline__ void issue_copy(uint32_t dst, const uint16_t* src, int kv0, int N,
                                            int wave, int lane) {
   using C = Cfg<D, NW>;
   const int rows = min(BC, N - kv0);
@@ -99,7 +100,7 @@ __device__ __forceinline__ void issue_copy(char* dst, const uint16_t* src, int k
     const int row = blk * C::RPB + lane / C::CPR;
     const int pos = lane % C::CPR;
     const int sw = IS_V ? vswz<D>(row) : kswz<D>(row);
-    dma16(desc, dst + blk * 1024, row * C::ROWB + ((pos ^ sw) << 4));
+    dma16(desc, dst + static_cast<uint32_t>(blk * 1024), row * C::ROWB + ((pos ^ sw) << 4));
   }
 }
 
@@ -500,9 +501,10 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   if (q0w < N) last = causal ? min(ntiles - 1, (q0w + BRW - 1) / BC) : ntiles - 1;
 
   // ---- prologue: K0, V0, K1 and Q in flight; scores of tile 0 ----
-  issue_copy<D, NW, false>(kring, kbase, 0, N, wave, lane);
-  issue_copy<D, NW, true>(vring, vbase, 0, N, wave, lane);
-  if (ntiles > 1) issue_copy<D, NW, false>(kring + C::TILEB, kbase, BC, N, wave, lane);
+  const uint32_t kring_a = lds_addr(kring), vring_a = lds_addr(vring);   // LDS byte addresses
+  issue_copy<D, NW, false>(kring_a, kbase, 0, N, wave, lane);
+  issue_copy<D, NW, true>(vring_a, vbase, 0, N, wave, lane);
+  if (ntiles > 1) issue_copy<D, NW, false>(kring_a + C::TILEB, kbase, BC, N, wave, lane);
   {
     const int rows = max(0, min(BRW, N - q0w));
     const auto rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -537,8 +539,8 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                        bf16x8& penext, float& lecur, float& lenext) {
     const char* kst_next = kring + ((t + 1) & 1) * C::TILEB;
     const char* vst = vring + (t & 1) * C::TILEB;
-    if (t + 1 < ntiles) issue_copy<D, NW, true>(vring + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave, lane);
-    if (t + 2 < ntiles) issue_copy<D, NW, false>(kring + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
+    if (t + 1 < ntiles) issue_copy<D, NW, true>(vring_a + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave, lane);
+    if (t + 2 < ntiles) issue_copy<D, NW, false>(kring_a + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
     if (t < last) {
       const int kv0n = (t + 1) * BC;
       float ll;

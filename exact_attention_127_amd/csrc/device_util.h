@@ -27,18 +27,26 @@ __device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
                static_cast<int>(bytes), 0x00020000};
 }
 
-// One 16-byte-per-lane HBM -> LDS copy: lane i's 16 bytes land at
-// lds_block + 16*i.  Issued as inline assembly so the compiler does not
-// serialise it against unrelated LDS reads; completion is tracked by the
+// 32-bit LDS byte address of a pointer into a __shared__ array, made
+// wave-uniform (an SGPR value).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(as_lds(p))));
+}
+
+// One 16-byte-per-lane HBM -> LDS copy: lane i's 16 bytes land at LDS byte
+// address lds_block + 16*i.  Issued as inline assembly so the compiler does
+// not serialise it against unrelated LDS reads; completion is tracked by the
 // explicit vmcnt waits of the tile loop.
-__device__ __forceinline__ void dma16(const i32x4& desc, const char* lds_block, int voffset) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(as_lds(lds_block))));
+__device__ __forceinline__ void dma16(const i32x4& desc, uint32_t lds_block, int voffset) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_block);   // uniform by construction
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m), "v"(voffset), "s"(desc) : "memory", "m0");
 #pragma clang diagnostic pop
+}
+__device__ __forceinline__ void dma16(const i32x4& desc, const char* lds_block, int voffset) {
+  dma16(desc, lds_addr(lds_block), voffset);
 }
 
 // Wait until at most n of this wave's vector-memory operations are in
