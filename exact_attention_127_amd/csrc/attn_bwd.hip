@@ -26,6 +26,8 @@
 // K, V, Q and dO tiles are each read both row-wise (16-byte reads) and
 // transposed (ds_read_b64_tr_b16); one XOR swizzle of the 16-byte chunks
 // keeps both patterns free of LDS bank conflicts.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -37,6 +39,7 @@ namespace {
 
 constexpr int BT = 64;        // rows per streamed tile (keys in dQ, queries in dK/dV)
 constexpr int kXcdsB = 8;     // XCDs the dispatcher round-robins over
+constexpr int kRingB = 3;     // K (and V) tiles resident in the dQ kernel's LDS
 
 template <int D>
 struct BTile {
@@ -186,7 +189,19 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const uint16_t* __restri
 #endif
 }
 
-// ---- dQ: query-major, K/V tiles streamed through two-slot rings ----
+// ---- dQ: query-major, K/V tiles streamed through three-slot rings ----
+//
+// Per 32-key block b of the wave: A_b = the products S^T = K Q^T and
+// dP^T = V dO^T (16 MFMAs at d=128), V_b = the vector work dS^T = P^T
+// (dP^T - D) with P^T = exp2(S^T c - LSE) (8 pairs of scores per lane),
+// C_b = dQ^T += K^T dS^T (8 MFMAs).  The blocks are software-pipelined: phase
+// b runs A_{b+1} slot by slot beside V_b (one MFMA, its operand read two
+// ahead and a share of the vector work per slot, closed by a scheduling
+// barrier; empty asm uses keep the vector work in its slot), then C_b.  So
+// the matrix cores and the vector ALU work side by side in one wave, where
+// the eight waves, held in step by the per-tile barrier, would otherwise all
+// wait on the same unit.  Tile t carries blocks 2t and 2t+1; iteration t runs
+// phases 2t-1 and 2t, which read K of tiles t-1 and t, hence three K slots.
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -198,9 +213,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   using T = BTile<D>;
   constexpr int BR = NW * 32;
   const bool causal = causal_arg != 0;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::TILEB];
-  char* const kring = smem;
-  char* const vring = smem + 2 * T::TILEB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kRingB * T::TILEB];   // K ring, then V ring
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
 
   // work item: whole heads per XCD, heaviest causal query blocks first
@@ -226,9 +239,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   const int kend = causal ? min(N, q0 + BR) : N;
   const int ntiles = (kend + BT - 1) / BT;
+  // last 32-key block this wave needs (-1: its rows are all past the end)
+  int lb = -1;
+  if (q0w < N) lb = causal ? min((N - 1) / 32, (q0w + 31) / 32) : (N - 1) / 32;
+  auto kslot = [&](int r) __attribute__((always_inline)) -> const char* { return smem + r * T::TILEB; };           // r = tile % 3
+  auto vslot = [&](int r) __attribute__((always_inline)) -> const char* { return smem + (kRingB + r) * T::TILEB; };
   if (ntiles > 0) {
-    copy_tile<D, NW>(kring, kbase, 0, N, wave, lane);
-    copy_tile<D, NW>(vring, vbase, 0, N, wave, lane);
+    copy_tile<D, NW>(smem, kbase, 0, N, wave, lane);
+    copy_tile<D, NW>(smem + kRingB * T::TILEB, vbase, 0, N, wave, lane);
   }
   // this lane's Q and dO row as B operands (rows past N read as zero)
   bf16x8 qr[D / 16], dor[D / 16];
@@ -256,47 +274,106 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   wait_vmcnt<0>();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const char* kst = kring + (t & 1) * T::TILEB;
-    const char* vst = vring + (t & 1) * T::TILEB;
-    if (t + 1 < ntiles) {
-      copy_tile<D, NW>(kring + ((t + 1) & 1) * T::TILEB, kbase, (t + 1) * BT, N, wave, lane);
-      copy_tile<D, NW>(vring + ((t + 1) & 1) * T::TILEB, vbase, (t + 1) * BT, N, wave, lane);
+  constexpr int NA = 2 * (D / 16);              // MFMAs of A (S^T, then dP^T)
+  constexpr int NC = 2 * (D / 32);              // MFMAs of C
+  // A operand of MFMA i of block b: a K row (S^T) or a V row (dP^T)
+  auto a_op = [&](const char* kst, const char* vst, int kb, int i) __attribute__((always_inline)) {
+    return i < D / 16 ? lds_row(kst + kb * 32 * T::ROWB + la.rofs[i])
+                      : lds_row(vst + kb * 32 * T::ROWB + la.rofs[i - D / 16]);
+  };
+  auto a_mfma = [&](f32x16& sacc, f32x16& dpacc, const bf16x8& a, int i) __attribute__((always_inline)) {
+    if (i < D / 16) sacc = mfma(a, qr[i], i == 0 ? f32x16{} : sacc);
+    else dpacc = mfma(a, dor[i - D / 16], i == D / 16 ? f32x16{} : dpacc);
+  };
+  // keys of block b past the sequence end or (causal) past this lane's row
+  // get S = -inf, so P = 0 and dS = 0 there
+  auto mask_block = [&](f32x16& sacc, int b) __attribute__((always_inline)) {
+    const int base_key = 32 * b + 4 * h;
+    const int lim = causal ? min(N - 1, qrow) - base_key : N - 1 - base_key;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = (8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : sacc[r];
+  };
+  auto needs_mask = [&](int b) __attribute__((always_inline)) { return (causal && 32 * b + 31 > q0w) || 32 * b + 32 > N; };
+  // dS^T for pair pr (accumulator registers 2pr, 2pr+1) into operand word dsw
+  auto ds_pair = [&](uint32_t (&dsw)[2][4], const f32x16& sacc, const f32x16& dpacc, int pr) __attribute__((always_inline)) {
+    const int r = 2 * pr;
+    const float d0 = fast_exp2(fmaf(sacc[r], c, -lse2)) * (dpacc[r] - dl);
+    const float d1 = fast_exp2(fmaf(sacc[r + 1], c, -lse2)) * (dpacc[r + 1] - dl);
+    dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(d0, d1);
+  };
+  auto c_mfmas = [&](const uint32_t (&dsw)[2][4], const char* kst, int kb) __attribute__((always_inline)) {
+    bf16x8 ktr[NC];
+    ktr[0] = lds_trans<D>(kst, la, 0, 2 * kb);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if (i + 1 < NC) ktr[i + 1] = lds_trans<D>(kst, la, (i + 1) % (D / 32), 2 * kb + (i + 1) / (D / 32));
+      const int cg = i / (D / 32), db = i % (D / 32);
+      const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dsw[cg][0], dsw[cg][1], dsw[cg][2], dsw[cg][3]});
+      acc[db] = mfma(ktr[i], dsb, acc[db]);
     }
+  };
+  auto pin = [](auto x) __attribute__((always_inline)) { asm volatile("" ::"v"(x)); };
+  // phase b: A_{b+1} beside V_b, then C_b.  (sc, dpc): products of block b;
+  // (sn, dpn): receive those of block b+1.  ks*/vs*: LDS tiles of the two blocks.
+  auto phase = [&](int b, auto kbc, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn,
+                   const char* kst_b, const char* kst_n, const char* vst_n) __attribute__((always_inline)) {
+    constexpr int kb = decltype(kbc)::value, kbn = 1 - kb;   // b & 1, (b + 1) & 1
+    const bool do_a = b + 1 <= lb, do_vc = b >= 0 && b <= lb;
+    uint32_t dsw[2][4];
+    if (do_vc && needs_mask(b)) mask_block(sc, b);
+    if (do_a && do_vc) {
+      bf16x8 aop[NA];
+      __builtin_amdgcn_sched_barrier(0);
+      aop[0] = a_op(kst_n, vst_n, kbn, 0);
+      aop[1] = a_op(kst_n, vst_n, kbn, 1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key0 = t * BT + kb * 32;
-      if (key0 >= N || (causal && key0 > q0w + 31)) continue;   // wave-uniform
-      f32x16 s = f32x16{}, dp = f32x16{};
+      for (int i = 0; i < NA; ++i) {
+        if (i + 2 < NA) aop[i + 2] = a_op(kst_n, vst_n, kbn, i + 2);
+        a_mfma(sn, dpn, aop[i], i);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        s = mfma(lds_row(kst + kb * 32 * T::ROWB + la.rofs[ks]), qr[ks], s);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        dp = mfma(lds_row(vst + kb * 32 * T::ROWB + la.rofs[ks]), dor[ks], dp);
-      // dS^T = P^T (dP^T - D), keys of this lane in accumulator-row order
-      uint32_t dsw[2][4];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float ds[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int key = key0 + 8 * ((r + x) >> 2) + 4 * h + ((r + x) & 3);
-          const bool masked = (key >= N) || (causal && key > qrow);
-          const float p = masked ? 0.f : fast_exp2(fmaf(s[r + x], c, -lse2));
-          ds[x] = p * (dp[r + x] - dl);
+        for (int pr = 0; pr < 8; ++pr) {
+          if ((pr * NA) / 8 != i) continue;
+          ds_pair(dsw, sc, dpc, pr);
+          pin(dsw[pr >> 2][pr & 3]);
         }
-        dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(ds[0], ds[1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      c_mfmas(dsw, kst_b, kb);
+    } else if (do_a) {
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) {
-        const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dsw[cg][0], dsw[cg][1], dsw[cg][2], dsw[cg][3]});
+      for (int i = 0; i < NA; ++i) a_mfma(sn, dpn, a_op(kst_n, vst_n, kbn, i), i);
+    } else if (do_vc) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] = mfma(lds_trans<D>(kst, la, db, 2 * kb + cg), dsb, acc[db]);
-      }
+      for (int pr = 0; pr < 8; ++pr) ds_pair(dsw, sc, dpc, pr);
+      c_mfmas(dsw, kst_b, kb);
     }
+  };
+
+  // iteration t (R = t mod 3, a compile-time slot index): copy tile t+1,
+  // run phases 2t-1 (A of block 2t, C of block 2t-1) and 2t (A of block
+  // 2t+1, C of block 2t)
+  f32x16 se = f32x16{}, dpe = f32x16{}, so = f32x16{}, dpo = f32x16{};   // even / odd blocks
+  auto iteration = [&](int t, auto rc) __attribute__((always_inline)) {
+    constexpr int R = decltype(rc)::value;
+    constexpr int RP = (R + 2) % 3, RN = (R + 1) % 3;
+    if (t + 1 < ntiles) {
+      copy_tile<D, NW>(smem + RN * T::TILEB, kbase, (t + 1) * BT, N, wave, lane);
+      copy_tile<D, NW>(smem + (kRingB + RN) * T::TILEB, vbase, (t + 1) * BT, N, wave, lane);
+    }
+    phase(2 * t - 1, std::integral_constant<int, 1>{}, so, dpo, se, dpe, kslot(RP), kslot(R), vslot(R));
+    phase(2 * t, std::integral_constant<int, 0>{}, se, dpe, so, dpo, kslot(R), kslot(R), vslot(R));
     wait_vmcnt<0>();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 3) {
+    iteration(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) iteration(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < ntiles) iteration(t + 2, std::integral_constant<int, 2>{});
+  }
+  // the last block's vector work and C (its tile is still in LDS)
+  if (ntiles > 0) {
+    const int r = (ntiles - 1) % 3;
+    phase(2 * ntiles - 1, std::integral_constant<int, 1>{}, so, dpo, se, dpe, kslot(r), kslot(r), vslot(r));
   }
   if (qrow < N) store_rows<D>(dq + base + static_cast<int64_t>(qrow) * D, acc, h, scale);
 #endif  // __HIP_DEVICE_COMPILE__
