@@ -452,12 +452,22 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       dma4(uniform_desc(delta + sbase + qt * BT, bytes), sring + slot * SB + BT * 4, lane * 4);
     }
   };
+  // wave 0 copied a tile's LSE row; once it has landed, the same wave turns
+  // it into base-2 units in place (one multiply per query instead of one per
+  // score), before the barrier that publishes the tile
+  auto lse_to_base2 = [&](int slot) {
+    if (wave == 0) {
+      float* l = reinterpret_cast<float*>(sring + slot * SB);
+      l[lane] *= kLog2e;
+    }
+  };
   if (qt0 < nqt) copy_qtile(qt0, 0);
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) { dka[db] = f32x16{}; dva[db] = f32x16{}; }
   const BLane<D> la(j, h, lane);
   wait_vmcnt<0>();
+  if (qt0 < nqt) lse_to_base2(0);
   __syncthreads();
 
   for (int qt = qt0; qt < nqt; ++qt) {
@@ -477,7 +487,19 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
         dp = mfma(lds_row(dst + sb * 32 * T::ROWB + la.rofs[ks]), lds_row(vw + la.rofs[ks]), dp);
-      // P and dS for this lane's key and the 16 queries 8g + 4h + (0..3)
+      // Only sub-blocks that reach the causal diagonal or the sequence end
+      // (wave-uniform test) carry a mask: the score becomes -inf there, so P
+      // and dS are exactly 0.
+      if ((qs + 31 >= N) || (k0w + 31 >= N) || (causal && k0w + 31 > qs)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qq = qs + 8 * (r >> 2) + 4 * h + (r & 3);
+          const bool masked = (qq >= N) || (key >= N) || (causal && key > qq);
+          s[r] = masked ? -INFINITY : s[r];
+        }
+      }
+      // P and dS for this lane's key and the 16 queries 8g + 4h + (0..3);
+      // the tile's LSE values were turned into base-2 units in LDS
       uint32_t pw[2][4], dsw[2][4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -487,9 +509,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = 4 * g + x;
-          const int qq = qs + 8 * g + 4 * h + x;
-          const bool masked = (qq >= N) || (key >= N) || (causal && key > qq);
-          pv[x] = masked ? 0.f : fast_exp2(fmaf(s[r], c, -lg[x] * kLog2e));
+          pv[x] = fast_exp2(fmaf(s[r], c, -lg[x]));
           dsv[x] = pv[x] * (dp[r] - dg[x]);
         }
         pw[g >> 1][(g & 1) * 2 + 0] = pack_bf16x2(pv[0], pv[1]);
@@ -509,6 +529,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
     wait_vmcnt<0>();
+    if (qt + 1 < nqt) lse_to_base2(slot ^ 1);
     __syncthreads();
   }
   if (key < N) {
