@@ -501,8 +501,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       // P and dS for this lane's key and the 16 queries 8g + 4h + (0..3);
       // the tile's LSE values were turned into base-2 units in LDS
       uint32_t pw[2][4], dsw[2][4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      auto group = [&](int g) __attribute__((always_inline)) {
         const f32x4 lg = *reinterpret_cast<const f32x4*>(sst + (sb * 32 + 8 * g + 4 * h) * 4);
         const f32x4 dg = *reinterpret_cast<const f32x4*>(sst + BT * 4 + (sb * 32 + 8 * g + 4 * h) * 4);
         float pv[4], dsv[4];
@@ -516,15 +515,28 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         pw[g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
         dsw[g >> 1][(g & 1) * 2 + 0] = pack_bf16x2(dsv[0], dsv[1]);
         dsw[g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
-      }
+      };
+      group(0);
+      group(1);
+      // dV and dK of the first operand half (queries of groups 0, 1), slot
+      // by slot beside groups 2 and 3 (one group per four MFMAs; empty asm
+      // uses keep that work in its slot), then the second half
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) {
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[cg][0], pw[cg][1], pw[cg][2], pw[cg][3]});
         const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dsw[cg][0], dsw[cg][1], dsw[cg][2], dsw[cg][3]});
+        if (cg == 0) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           dva[db] = mfma(lds_trans<D>(dst, la, db, 2 * sb + cg), pb, dva[db]);
           dka[db] = mfma(lds_trans<D>(qst, la, db, 2 * sb + cg), dsb, dka[db]);
+          if (cg == 0 && (db == 0 || db == D / 64)) {
+            const int g = db == 0 ? 2 : 3;
+            group(g);
+            asm volatile("" ::"v"(pw[1][(g & 1) * 2]), "v"(pw[1][(g & 1) * 2 + 1]),
+                         "v"(dsw[1][(g & 1) * 2]), "v"(dsw[1][(g & 1) * 2 + 1]));
+          }
+          if (cg == 0) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
