@@ -207,3 +207,26 @@ def test_fp8_workload_literal(gpu):
         floor_a = max(floor_a, float(np.abs(ob[i] - oa).max()))
     print(f"fp8 literal, full GPU pipeline vs unquantised oracle: max-abs {worst_a:.3f} "
           f"(input-quantisation floor {floor_a:.3f})")
+
+
+@pytest.mark.parametrize("rise", [3.0, 20.0, 100.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_rising_scores(gpu, rise, causal):
+    """Scores that grow along the keys (3, 20 and 100 per 64 keys): each key
+    tile's numerators outgrow the exponent reference of earlier tiles, so the
+    kernel must move it to the tile's own maximum again and again."""
+    from tests.test_parity_gpu import _rising_inputs
+    d, N = 128, 300
+    inp = _rising_inputs(N, d, causal, rise, seed=int(rise) + 7 * causal)
+    R = haar_orthogonal(np.random.default_rng(5).standard_normal((d, d))).astype(np.float32)
+    cs = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], R)
+    o, lse = _fwd_on_codes(cs, gpu, inp["scale"], causal)
+    heads = [(0, h) for h in range(2)]
+    rows = np.arange(N)
+    ob, lb = _oracle_b(cs, heads, rows, inp["scale"], causal)
+    od = np.stack([o[b, h] for b, h in heads])
+    ld = np.stack([lse[b, h] for b, h in heads])
+    assert np.isfinite(od).all() and np.isfinite(ld).all()
+    assert np.all(np.abs(od - ob) <= TOL8 * np.maximum(1.0, np.abs(ob)))
+    assert np.abs(od - ob).mean() < 5e-3
+    assert np.max(np.abs(ld - lb)) < 2e-2
