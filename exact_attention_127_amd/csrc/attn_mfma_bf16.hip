@@ -7,8 +7,8 @@
 // the grid, so even one head fills the machine at long sequence length --
 // and an inner loop over key/value tiles of BC keys.  Per tile:
 //   S^T = K Q^T        bf16 MFMA 32x32x16, float32 accumulate
-//   online softmax     running row maximum m and normaliser l in registers,
-//                      p = exp2(S*c - m) with c = scale*log2(e)
+//   online softmax     exponent reference m and normaliser l per row in
+//                      registers, p = exp2(S*c - m) with c = scale*log2(e)
 //   O^T += V^T P^T     P rounded to bf16, bf16 MFMA, float32 accumulate
 // and after the last tile O /= l once, O rounded to bf16, LSE = ln2*(m+log2 l).
 // S and P live only in registers; nothing N x N reaches memory.
@@ -16,18 +16,20 @@
 // gfx950 mapping:
 //  * Scores are computed transposed (keys x queries): in the 32x32
 //    accumulator layout each lane then holds 16 keys of ONE query (column
-//    lane%32), so the row maximum and row sum are in-lane reductions plus one
-//    v_permlane32_swap between the two lane halves.
+//    lane%32), so row reductions (the first tile's maximum, the sum) are
+//    in-lane reductions plus one v_permlane32_swap between the lane halves.
 //  * Those probabilities feed the second product directly as its B operand;
 //    its A operand (V^T) comes from row-major V in LDS through
 //    ds_read_b64_tr_b16, which hands each lane four keys of one channel, read
 //    in exactly the key order the accumulator registers hold.
-//  * Each wave software-pipelines its tiles: while the matrix cores compute
-//    the scores of tile t+1, the vector ALUs run the exponentials of tile t;
-//    while they compute P V of tile t, the vector ALUs take the row maximum
-//    of tile t+1.  The two streams are interleaved instruction by instruction
-//    (scheduling groups), which is what lets MFMA and VALU work overlap
-//    inside one wave.
+//  * Each wave software-pipelines its tiles in two phases: while the matrix
+//    cores compute the scores of tile t+1, the vector ALUs run the
+//    exponentials of tile t's first three P operands; while they compute P V
+//    of tile t, the vector ALUs scale tile t+1's scores into exponents and
+//    form its last P operand.  Both phases are written slot by slot (one
+//    MFMA, its operand read and a share of the vector work per slot, closed
+//    by a scheduling barrier and pinned by empty asm uses), which is what
+//    lets MFMA and VALU work overlap inside one wave.
 //  * K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16
 //    bytes per lane, no register staging) in two-slot rings: K of tile t+2
 //    and V of tile t+1 are copied while tile t is processed; one barrier per
@@ -39,10 +41,11 @@
 //    the normaliser and the partial output carry the same reference, and the
 //    single division at the end cancels it exactly.  Most tiles of a long
 //    row therefore skip both the maximum and the rescale.
-//  * Two workgroups share a CU (one wave of each per SIMD), so one hides the
-//    other's barrier and copy waits.  Work items are grouped by XCD
-//    (dispatch is round-robin over the 8 XCDs) so the query blocks of one
-//    head share one L2, heaviest causal blocks first.
+//  * d=128: one workgroup of eight waves (two per SIMD) per CU shares each
+//    K/V tile over 256 query rows; d=64: two workgroups of four waves per
+//    CU.  Work items are grouped by XCD (dispatch is round-robin over the 8
+//    XCDs) so the query blocks of one head share one L2, heaviest causal
+//    blocks first.
 #include "common.h"
 #include "launch.h"
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -62,8 +62,10 @@ typedef enum {
  * attn_fwd -- O = softmax(Q K^T * scale) V and LSE for all B*H heads.
  *
  * dtype ATTN_BF16 runs the matrix-core kernel: both products on bf16 MFMA
- * with float32 accumulation, the online softmax (running row maximum and
- * running normaliser, the partial output rescaled as each key tile arrives;
+ * with float32 accumulation, the online softmax (a running normaliser and a
+ * per-row exponent reference -- the first key tile's maximum, moved to a
+ * later tile's maximum only when that tile's numerators would grow past
+ * 2^16 -- with the partial output rescaled whenever the reference moves;
  * page "Self-Attention, CUDA kernels and FlashAttention", section 3) in
  * float32, P rounded to bf16 (nearest-even) as the second product's operand,
  * the 1/normaliser division done once after the last key tile (page
