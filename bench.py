@@ -360,7 +360,7 @@ def main() -> int:
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward pass (default) or the backward pass (bf16 workloads)")
     ap.add_argument("--fp8-scales", choices=("tile", "mx"), default="tile",
-                    help="fp8 workloads: one float32 scale per 64-row tile (default) or one "
+                    help="fp8 workloads: one float32 scale per 128-token tile (default) or one "
                          "power-of-two scale per 32 channels of a token (MXFP8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
