@@ -55,7 +55,7 @@ def _check(name, g, r, max_tol=REL_MAX, mean_tol=REL_MEAN):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [2, 31, 64, 65, 127, 129, 200, 300])
+@pytest.mark.parametrize("N", [2, 31, 64, 65, 127, 129, 200, 300, 449, 700])
 def test_small_shapes_match_the_oracle(gpu, N, d, causal):
     inp = random_inputs(1, 2, N, d, "bf16", causal, seed=300 + N + d + causal)
     do = make_output_grad(inp["workload"])
