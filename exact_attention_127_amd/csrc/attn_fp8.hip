@@ -33,15 +33,18 @@ constexpr int kTile8 = kFp8Tile;     // tokens per quantisation tile
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-constexpr int NW8 = 4;               // waves per workgroup
+// NW waves per workgroup, 32 query rows each.  Per-tile scales at d=128 take
+// 8 (256 rows share every copied and widened K/V tile; one workgroup per CU).
+// MXFP8 keeps 4 with two workgroups per CU: its per-block scale work on the
+// vector ALU then runs beside the other workgroup's matrix work, which pays
+// more than sharing the tiles (measured: 8 waves ran 27% slower there).  d=64
+// keeps 4 (its 4 KB fp8 tile splits over at most four waves).
 constexpr int kXcds8 = 8;            // XCDs the dispatcher round-robins over
-constexpr int BR8 = NW8 * 32;        // query rows per workgroup (one quantisation tile)
 constexpr int BC8 = 64;              // keys per tile (half a quantisation tile)
-constexpr int NT8 = NW8 * 64;
 constexpr float kTau8 = 8.0f;        // p <= 2^kTau8 (exponent reference raised lazily)
-static_assert(BR8 == kTile8, "a workgroup's rows share one Q scale");
+static_assert(kTile8 % 32 == 0, "a wave's 32 rows share one Q scale");
 
-template <int D>
+template <int D, int NW>
 struct Cfg8 {
   static constexpr int ROWB = D;               // bytes per fp8 K/V row
   static constexpr int ROWB16 = 2 * D;         // bytes per bf16 V row
@@ -50,8 +53,8 @@ struct Cfg8 {
   static constexpr int TILEB = BC8 * ROWB;     // fp8 tile
   static constexpr int TILEB16 = BC8 * ROWB16; // bf16 V tile
   static constexpr int BLK = TILEB / 1024;
-  static constexpr int BPW = BLK / NW8;
-  static_assert(BPW * NW8 == BLK, "tile must split evenly over the waves");
+  static constexpr int BPW = BLK / NW;
+  static_assert(BPW * NW == BLK, "tile must split evenly over the waves");
 };
 
 // fp8 rows: chunk swizzle spreading the rows that one K operand read touches
@@ -67,9 +70,9 @@ __device__ __forceinline__ int swz16(int row) { return D == 128 ? ((row & 3) << 
 #if defined(__HIP_DEVICE_COMPILE__)
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void issue_copy8(char* dst, const uint8_t* src, int kv0, int N, int wave, int lane) {
-  using C = Cfg8<D>;
+  using C = Cfg8<D, NW>;
   const int rows = min(BC8, N - kv0);
   const i32x4 desc = buffer_desc(src + static_cast<int64_t>(kv0) * D, static_cast<uint32_t>(rows) * C::ROWB);
 #pragma unroll
@@ -84,9 +87,9 @@ __device__ __forceinline__ void issue_copy8(char* dst, const uint8_t* src, int k
 // The blocks of a V tile this wave copied: e4m3 codes -> bf16 (exact), into
 // the bf16 tile.  Lane i's 16 codes are channels 16c..16c+15 of one row.
 // Row and channel chunk (16 codes) that lane `lane` converts in block b.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void convert_slot(int wave, int lane, int b, int& row, int& c) {
-  using C = Cfg8<D>;
+  using C = Cfg8<D, NW>;
   const int blk = wave * C::BPW + b;
   row = blk * C::RPB + lane / C::CPR;
   c = (lane % C::CPR) ^ swz8<D>(row);
@@ -94,15 +97,15 @@ __device__ __forceinline__ void convert_slot(int wave, int lane, int b, int& row
 
 // vscale[b]: the power of two multiplying block b's codes (1 for per-tile
 // scales, whose factor rides on P; 2^e of the 32-channel block for MXFP8).
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void convert_v(char* dst16, const char* src8, int wave, int lane,
-                                          const float (&vscale)[Cfg8<D>::BPW]) {
-  using C = Cfg8<D>;
+                                          const float (&vscale)[Cfg8<D, NW>::BPW]) {
+  using C = Cfg8<D, NW>;
 #pragma unroll
   for (int b = 0; b < C::BPW; ++b) {
     const int blk = wave * C::BPW + b;
     int row, c;
-    convert_slot<D>(wave, lane, b, row, c);
+    convert_slot<D, NW>(wave, lane, b, row, c);
     const u32x4 x = *reinterpret_cast<const u32x4*>(src8 + blk * 1024 + lane * 16);
     const float sc = vscale[b];
     u32x4 lo, hi;
@@ -148,15 +151,15 @@ __device__ __forceinline__ uint32_t load_row_scales(__amdgpu_buffer_rsrc_t r, in
 // codes are one block), V is widened to bf16 with its block scale (exact),
 // and P carries no scale.  Each lane loads the scale bytes it needs with the
 // tile copies, so they are covered by the same wait.
-template <int D, bool CAUSAL, bool MX>
-__global__ void __launch_bounds__(NT8, 2)
+template <int D, int NW, bool CAUSAL, bool MX>
+__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
                 const uint8_t* __restrict__ v8, const void* __restrict__ sqv,
                 const void* __restrict__ skv, const void* __restrict__ svv,
                 uint16_t* __restrict__ o, float* __restrict__ lse, int N, int BH, int nqb,
                 int ntq, float c0, int hc) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = Cfg8<D>;
+  using C = Cfg8<D, NW>;
   __shared__ __attribute__((aligned(1024))) char kring[2 * C::TILEB];     // fp8 K, two slots
   __shared__ __attribute__((aligned(1024))) char vstage[C::TILEB];        // fp8 V landing area
   __shared__ __attribute__((aligned(1024))) char vring[2 * C::TILEB16];   // bf16 V, two slots
@@ -185,7 +188,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   } else {
     bh = id / nqb; qbk = id % nqb;
   }
-  const int q0 = qbk * BR8;
+  const int q0 = qbk * (NW * 32);
   const int q0w = q0 + wave * 32;
   const int qrow = q0w + j;
   const int64_t base = static_cast<int64_t>(bh) * N * D;
@@ -195,7 +198,8 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   // multiplier s_q * scale * log2(e); MXFP8: per-head scale arrays
   const float* skh = MX ? nullptr : static_cast<const float*>(skv) + static_cast<int64_t>(bh) * ntq;
   const float* svh = MX ? nullptr : static_cast<const float*>(svv) + static_cast<int64_t>(bh) * ntq;
-  const float cq = MX ? c0 : c0 * static_cast<const float*>(sqv)[static_cast<int64_t>(bh) * ntq + q0 / kTile8];
+  // the Q tile scale of this wave's rows (a wave past the end reads the last tile's)
+  const float cq = MX ? c0 : c0 * static_cast<const float*>(sqv)[static_cast<int64_t>(bh) * ntq + min(q0w, N - 1) / kTile8];
   constexpr int SPR = D / 32;                    // scale bytes per row (MXFP8)
   const int64_t sbase = static_cast<int64_t>(bh) * N * SPR;
   const auto rks = __builtin_amdgcn_make_buffer_rsrc(
@@ -203,37 +207,37 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   const auto rvs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(static_cast<const uint8_t*>(svv) + (MX ? sbase : 0)), 0, MX ? N * SPR : 0, 0x00020000);
   uint32_t kscw[2] = {0u, 0u};                   // this lane's K row scales, current tile
-  float vsc[Cfg8<D>::BPW];                       // V block scales of the tile being converted
-  auto load_tile_scales = [&](int kv0n, uint32_t (&kw)[2], float (&vs)[Cfg8<D>::BPW]) {
+  float vsc[Cfg8<D, NW>::BPW];                       // V block scales of the tile being converted
+  auto load_tile_scales = [&](int kv0n, uint32_t (&kw)[2], float (&vs)[Cfg8<D, NW>::BPW]) {
     if constexpr (MX) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) kw[kb] = load_row_scales<D>(rks, kv0n + kb * 32 + j);
 #pragma unroll
-      for (int b = 0; b < Cfg8<D>::BPW; ++b) {
+      for (int b = 0; b < Cfg8<D, NW>::BPW; ++b) {
         int row, cch;
-        convert_slot<D>(wave, lane, b, row, cch);
+        convert_slot<D, NW>(wave, lane, b, row, cch);
         const uint32_t e = __builtin_amdgcn_raw_buffer_load_b8(rvs, (kv0n + row) * SPR + cch / 2, 0, 0);
         vs[b] = static_cast<float>(e);           // exponent byte; widened after the wait
       }
     } else {
 #pragma unroll
-      for (int b = 0; b < Cfg8<D>::BPW; ++b) vs[b] = 1.f;
+      for (int b = 0; b < Cfg8<D, NW>::BPW; ++b) vs[b] = 1.f;
     }
   };
-  auto widen = [&](float (&vs)[Cfg8<D>::BPW]) {
+  auto widen = [&](float (&vs)[Cfg8<D, NW>::BPW]) {
     if constexpr (MX) {
 #pragma unroll
-      for (int b = 0; b < Cfg8<D>::BPW; ++b) vs[b] = ldexpf(1.f, static_cast<int>(vs[b]) - 127);
+      for (int b = 0; b < Cfg8<D, NW>::BPW; ++b) vs[b] = ldexpf(1.f, static_cast<int>(vs[b]) - 127);
     }
   };
 
-  const int kend = CAUSAL ? min(N, q0 + BR8) : N;
+  const int kend = CAUSAL ? min(N, q0 + NW * 32) : N;
   const int ntiles = (kend + BC8 - 1) / BC8;
   int last = -1;
   if (q0w < N) last = CAUSAL ? min(ntiles - 1, (q0w + 31) / BC8) : ntiles - 1;
 
-  issue_copy8<D>(kring, kbase, 0, N, wave, lane);
-  issue_copy8<D>(vstage, vbase, 0, N, wave, lane);
+  issue_copy8<D, NW>(kring, kbase, 0, N, wave, lane);
+  issue_copy8<D, NW>(vstage, vbase, 0, N, wave, lane);
   load_tile_scales(0, kscw, vsc);
   // Q block scales of this lane's row, k-step ks: block 2 ks + h
   int qsc[D / 64];
@@ -270,7 +274,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   }
   wait_vmcnt<0>();
   widen(vsc);
-  convert_v<D>(vring, vstage, wave, lane, vsc);     // this wave's own copied blocks
+  convert_v<D, NW>(vring, vstage, wave, lane, vsc);     // this wave's own copied blocks
   __syncthreads();
 
   f32x16 oacc[D / 32];
@@ -296,8 +300,8 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
     const char* vst = vring + (t & 1) * C::TILEB16;
     uint32_t kscw_next[2] = {0u, 0u};
     if (t + 1 < ntiles) {
-      issue_copy8<D>(kring + ((t + 1) & 1) * C::TILEB, kbase, kv0 + BC8, N, wave, lane);
-      issue_copy8<D>(vstage, vbase, kv0 + BC8, N, wave, lane);
+      issue_copy8<D, NW>(kring + ((t + 1) & 1) * C::TILEB, kbase, kv0 + BC8, N, wave, lane);
+      issue_copy8<D, NW>(vstage, vbase, kv0 + BC8, N, wave, lane);
       load_tile_scales(kv0 + BC8, kscw_next, vsc);
     }
     if (t <= last) {
@@ -384,7 +388,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
       // previous barrier)
       wait_vmcnt<0>();
       widen(vsc);
-      convert_v<D>(vring + ((t + 1) & 1) * C::TILEB16, vstage, wave, lane, vsc);
+      convert_v<D, NW>(vring + ((t + 1) & 1) * C::TILEB16, vstage, wave, lane, vsc);
       kscw[0] = kscw_next[0];
       kscw[1] = kscw_next[1];
     }
@@ -411,14 +415,14 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool CAUSAL, bool MX>
+template <int D, int NW, bool CAUSAL, bool MX>
 hipError_t fwd_one(const Fp8Args& a) {
   const int BH = a.B * a.H;
-  const int nqb = (a.N + BR8 - 1) / BR8;
+  const int nqb = (a.N + NW * 32 - 1) / (NW * 32);
   const int ntq = (a.N + kTile8 - 1) / kTile8;
   const int64_t blocks = static_cast<int64_t>(nqb) * BH;
   const int hc = causal_head_chunk(BH, 2LL * a.N * D);      // fp8 K and V bytes of a head
-  hipLaunchKernelGGL((attn_fp8_kernel<D, CAUSAL, MX>), dim3(static_cast<unsigned>(blocks)), dim3(NT8), 0,
+  hipLaunchKernelGGL((attn_fp8_kernel<D, NW, CAUSAL, MX>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), 0,
                      static_cast<hipStream_t>(a.stream), a.q8, a.k8, a.v8, a.sq, a.sk, a.sv,
                      static_cast<uint16_t*>(a.o), a.lse, a.N, BH, nqb, ntq, a.scale * kLog2e, hc);
   return hipGetLastError();
@@ -428,11 +432,11 @@ hipError_t fwd_one(const Fp8Args& a) {
 
 hipError_t launch_fp8_fwd(const Fp8Args& a) {
   if (a.mx) {
-    if (a.d == 64) return a.causal ? fwd_one<64, true, true>(a) : fwd_one<64, false, true>(a);
-    return a.causal ? fwd_one<128, true, true>(a) : fwd_one<128, false, true>(a);
+    if (a.d == 64) return a.causal ? fwd_one<64, 4, true, true>(a) : fwd_one<64, 4, false, true>(a);
+    return a.causal ? fwd_one<128, 4, true, true>(a) : fwd_one<128, 4, false, true>(a);
   }
-  if (a.d == 64) return a.causal ? fwd_one<64, true, false>(a) : fwd_one<64, false, false>(a);
-  return a.causal ? fwd_one<128, true, false>(a) : fwd_one<128, false, false>(a);
+  if (a.d == 64) return a.causal ? fwd_one<64, 4, true, false>(a) : fwd_one<64, 4, false, false>(a);
+  return a.causal ? fwd_one<128, 8, true, false>(a) : fwd_one<128, 8, false, false>(a);
 }
 
 }  // namespace attn127
