@@ -127,7 +127,9 @@ def _fwd_on_codes(cs, gpu, scale, causal):
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("N", [1, 64, 129, 300])
+# N = 777 = 3*256 + 9 = 6*128 + 9: several full query blocks of 256 or 128
+# rows and a ragged last one, whose waves past the end hold no rows
+@pytest.mark.parametrize("N", [1, 64, 129, 300, 777])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_fp8_vs_dequantised_oracle(gpu, N, d, causal):

@@ -116,7 +116,9 @@ def _bound(cs, heads, rows, scale, causal):
     return np.stack(bs)
 
 
-@pytest.mark.parametrize("N", [1, 64, 129, 300])
+# N = 777 = 3*256 + 9 = 6*128 + 9: several full query blocks of 256 or 128
+# rows and a ragged last one, whose waves past the end hold no rows
+@pytest.mark.parametrize("N", [1, 64, 129, 300, 777])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_mxfp8_vs_dequantised_oracle(gpu, N, d, causal):
