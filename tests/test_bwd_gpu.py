@@ -66,6 +66,19 @@ def test_small_shapes_match_the_oracle(gpu, N, d, causal):
     _check(f"N={N} d={d} causal={causal} dv", dv, rv)
 
 
+# B*H a multiple of 8: the dK/dV and dQ grids give each XCD whole heads and,
+# when causal, walk chunks of heads; all gradients are compared
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_grouped_grid(gpu, causal):
+    inp = random_inputs(2, 8, 300, 128, "bf16", causal, seed=500 + causal)
+    do = make_output_grad(inp["workload"])
+    dq, dk, dv = _run(inp, do, gpu)
+    rq, rk, rv = oracle.attention_backward(inp["q"], inp["k"], inp["v"], do, inp["scale"], causal)
+    _check(f"B*H=16 causal={causal} dq", dq, rq)
+    _check(f"B*H=16 causal={causal} dk", dk, rk)
+    _check(f"B*H=16 causal={causal} dv", dv, rv)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_single_token_gradients(gpu, d):
     # one key: P = 1, so dS = 0 (dQ = dK = 0 up to float32 rounding of D) and dV = dO

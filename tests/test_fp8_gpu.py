@@ -147,6 +147,24 @@ def test_fwd_fp8_vs_dequantised_oracle(gpu, N, d, causal):
     assert np.max(np.abs(ld - lb)) < 2e-2
 
 
+# B*H a multiple of 8: whole heads per XCD, causal head chunks (every row compared)
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_head_grouped_grid(gpu, causal):
+    N, d = 777, 128
+    inp = random_inputs(2, 8, N, d, "f32", causal, seed=4100 + causal)
+    R = haar_orthogonal(np.random.default_rng(77).standard_normal((d, d))).astype(np.float32)
+    cs = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], R)
+    o, lse = _fwd_on_codes(cs, gpu, inp["scale"], causal)
+    rows = np.arange(N)
+    heads = [(b, h) for b in range(2) for h in range(8)]
+    ob, lb = _oracle_b(cs, heads, rows, inp["scale"], causal)
+    od = np.stack([o[b, h] for b, h in heads])
+    ld = np.stack([lse[b, h] for b, h in heads])
+    assert np.all(np.abs(od - ob) <= TOL8 * np.maximum(1.0, np.abs(ob)))
+    assert np.abs(od - ob).mean() < 5e-3
+    assert np.max(np.abs(ld - lb)) < 2e-2
+
+
 def _sample_heads(w, n, seed):
     rng = np.random.default_rng(seed)
     return sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(n)} | {(0, 0)})

@@ -56,6 +56,18 @@ def test_mfma_bf16_small(gpu, N, d, causal):
     _check_full(A.attn_fwd, inp, gpu, "bf16", small=True)
 
 
+# B*H a multiple of 8: the grid gives each XCD whole heads and, when causal,
+# walks chunks of heads heaviest query block first (chunks of 2 and 3 heads
+# here); every row is compared, so a work item mapped twice or never fails.
+@pytest.mark.parametrize("B,H", [(2, 8), (3, 8)])
+@pytest.mark.parametrize("N", [200, 777])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mfma_bf16_head_grouped_grid(gpu, B, H, N, d, causal):
+    inp = random_inputs(B, H, N, d, "bf16", causal, seed=400 + B + N + d + causal)
+    _check_full(A.attn_fwd, inp, gpu, "bf16", small=True)
+
+
 @pytest.mark.parametrize("N", SMALL_N)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
