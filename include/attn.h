@@ -120,11 +120,9 @@ int attn_fp8_prepare(const float* q, const float* k, const float* v,
  * Q K^T runs on fp8 MFMA (e4m3 x e4m3, float32 accumulation) with the Q and
  * K tile scales folded into the exponent's multiplier.  P V runs on bf16
  * MFMA: each e4m3 V tile is widened to bf16 (exact) in LDS, and P, carrying
- * the V tile's scale, is rounded to bf16 (nearest-even).  The normaliser
- * sums those rounded weights, so each O row is an exactly normalised
- * combination of V rows; lse is that sum's log (within 2^-8 relative of the
- * float32 sum in its argument).  o is bf16 [B][H][N][d]; lse (nullable)
- * float32 [B][H][N].  Other conventions as attn_fwd.
+ * the V tile's scale, is rounded to bf16 (nearest-even).  o is bf16
+ * [B][H][N][d]; lse (nullable) float32 [B][H][N].  Other conventions as
+ * attn_fwd.
  */
 int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  const float* q_scale, const float* k_scale,
