@@ -122,13 +122,6 @@ __device__ __forceinline__ void convert_v(char* dst16, const char* src8, int wav
   }
 }
 
-// acc + lo + hi of a packed bf16 pair (one dot product with (1, 1))
-__device__ __forceinline__ float sum_bf16x2(uint32_t pk, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
-                                         acc, false);
-}
-
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // operand formats 0/0 = e4m3; block scales 127 = 2^0
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -360,12 +353,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       }
       // operand p' = p * s_v = exp2(s*ct - m + log2 s_v); the normaliser
-      // takes sum(p') / s_v.  Per-tile scales: the sum is taken over the
-      // bf16-rounded p' that multiply V (one dot product per packed pair
-      // instead of two float32 additions), so O is an exactly normalised
-      // combination of V rows; the LSE moves by at most 2^-8 relative to its
-      // argument, far inside the fp8 path's quantisation error.  MXFP8 keeps
-      // the float32 sums.
+      // takes sum(p') / s_v
       const float svt = MX ? 1.f : svh[kv0 / kTile8];
       const float mref = ((m == -INFINITY) ? 0.f : m) - (MX ? 0.f : __log2f(svt));
       uint32_t pw[4][4];
@@ -376,16 +364,9 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
         for (int r = 0; r < 16; r += 2) {
           const float p0 = fast_exp2(fmaf(sacc[kb][r], ct, -mref));
           const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], ct, -mref));
-          const uint32_t pk = pack_bf16x2(p0, p1);
-          pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pk;
-          if constexpr (MX) {
-            ls0 += p0;
-            ls1 += p1;
-          } else if ((r & 2) == 0) {
-            ls0 = sum_bf16x2(pk, ls0);
-          } else {
-            ls1 = sum_bf16x2(pk, ls1);
-          }
+          ls0 += p0;
+          ls1 += p1;
+          pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
         }
       lsum += MX ? (ls0 + ls1) : (ls0 + ls1) / svt;
       // ---- O^T += V^T P'^T (bf16) ----
