@@ -35,10 +35,11 @@ constexpr int kTile8 = kFp8Tile;     // tokens per quantisation tile
 // ---------------------------------------------------------------------------
 // NW waves per workgroup, 32 query rows each.  Per-tile scales at d=128 take
 // 8 (256 rows share every copied and widened K/V tile; one workgroup per CU).
-// MXFP8 keeps 4 with two workgroups per CU: its per-block scale work on the
-// vector ALU then runs beside the other workgroup's matrix work, which pays
-// more than sharing the tiles (measured: 8 waves ran 27% slower there).  d=64
-// keeps 4 (its 4 KB fp8 tile splits over at most four waves).
+// MXFP8 keeps 4 with two workgroups per CU: 8 waves measured 27% slower
+// there, most likely because its per-block scale loads and widening then
+// stall all eight waves at each tile's barrier, where two independent
+// workgroups overlap that work with each other's matrix work.  d=64 keeps 4
+// (its 4 KB fp8 tile splits over at most four waves).
 constexpr int kXcds8 = 8;            // XCDs the dispatcher round-robins over
 constexpr int BC8 = 64;              // keys per tile (half a quantisation tile)
 constexpr float kTau8 = 8.0f;        // p <= 2^kTau8 (exponent reference raised lazily)
