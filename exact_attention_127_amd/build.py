@@ -2,8 +2,7 @@
 
 Each ``csrc/*.hip`` file is compiled to an object with hipcc (host and gfx950
 device code), then linked into one shared library next to this file.  Run as
-``python -m exact_attention_127_amd.build``; ``__graft_entry__.build()`` calls
-:func:`build`.
+``python -m exact_attention_127_amd.build``, or call :func:`build`.
 """
 from __future__ import annotations
 
