@@ -148,10 +148,11 @@ def test_fwd_fp8_vs_dequantised_oracle(gpu, N, d, causal):
 
 
 # B*H a multiple of 8: whole heads per XCD, causal head chunks (every row compared)
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fwd_fp8_head_grouped_grid(gpu, causal):
-    N, d = 777, 128
-    inp = random_inputs(2, 8, N, d, "f32", causal, seed=4100 + causal)
+def test_fwd_fp8_head_grouped_grid(gpu, d, causal):
+    N = 777
+    inp = random_inputs(2, 8, N, d, "f32", causal, seed=4100 + d + causal)
     R = haar_orthogonal(np.random.default_rng(77).standard_normal((d, d))).astype(np.float32)
     cs = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], R)
     o, lse = _fwd_on_codes(cs, gpu, inp["scale"], causal)

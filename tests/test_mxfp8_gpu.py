@@ -139,6 +139,25 @@ def test_fwd_mxfp8_vs_dequantised_oracle(gpu, N, d, causal):
     assert np.abs(ld - lb).max() <= 1e-3
 
 
+# B*H a multiple of 8: whole heads per XCD, causal head chunks (every row compared)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_mxfp8_head_grouped_grid(gpu, d, causal):
+    N = 777
+    inp = random_inputs(2, 8, N, d, "f32", causal, seed=4300 + d + causal)
+    R = haar_orthogonal(np.random.default_rng(79).standard_normal((d, d))).astype(np.float32)
+    cs = oracle.mxfp8_prepare(inp["q"], inp["k"], inp["v"], R)
+    o, lse = _fwd_on_codes(cs, gpu, inp["scale"], causal)
+    heads = [(b, h) for b in range(2) for h in range(8)]
+    rows = np.arange(N)
+    ob, lb = _oracle_b(cs, heads, rows, inp["scale"], causal)
+    od = np.stack([o[b, h] for b, h in heads])
+    ld = np.stack([lse[b, h] for b, h in heads])
+    bound = _bound(cs, heads, rows, inp["scale"], causal)
+    assert np.all(np.abs(od - ob) <= bound)
+    assert np.abs(ld - lb).max() <= 1e-3
+
+
 def _sample_heads(w, n, seed):
     rng = np.random.default_rng(seed)
     return sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(n)} | {(0, 0)})
