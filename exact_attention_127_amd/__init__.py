@@ -19,7 +19,6 @@ The functions keep the C names:
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch  # loads the HIP runtime that the library then shares
@@ -111,29 +110,63 @@ def _check(status: int, where: str):
         raise AttnError(status, where)
 
 
+def _scale_arg(scale):
+    """The scale passed to the C ABI: None selects the library's default,
+    1/sqrt(d), which the C side applies when it receives 0."""
+    return 0.0 if scale is None else float(scale)
+
+
+def _want(t, name, shape, dtype):
+    """A tensor argument must have exactly this shape and dtype and be
+    contiguous (the C ABI sees only a pointer, so it cannot check sizes)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_gpu(**tensors):
+    """Every tensor argument must live on one GPU: a host pointer handed to a
+    kernel would fault the device."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, not on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {dev}")
+
+
 def _fwd(name, q, k, v, o, lse, scale, causal, stream, with_lse):
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, N, d = q.shape
-    for t in (q, k, v):
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v must share shape, dtype and device")
-        if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous")
     if q.dtype == torch.bfloat16:
         dtype = ATTN_BF16
     elif q.dtype == torch.float32:
         dtype = ATTN_F32
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _want(t, nm, q.shape, q.dtype)
+    if o is not None:
+        _want(o, "o", q.shape, q.dtype)
+    if lse is not None:
+        _want(lse, "lse", (B, H, N), torch.float32)
+    _same_gpu(q=q, k=k, v=v, o=o, lse=lse)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
-                              float(scale), int(bool(causal)), dtype, _stream(stream))
+                              _scale_arg(scale), int(bool(causal)), dtype, _stream(stream))
     _check(st, name)
     return o, lse
 
@@ -151,12 +184,13 @@ def attn_fwd_simple(q, k, v, o=None, lse=None, scale=None, causal=False, stream=
 
 def attn_fp8_prepare(q, k, v, R, stream=None):
     """Rotate Q, K by R and quantise Q, K, V to e4m3 with one scale per 128-token tile."""
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, N, d = q.shape
-    for t in (q, k, v):
-        if t.shape != q.shape or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous float32 [B, H, N, d]")
-    if R.shape != (d, d) or R.dtype != torch.float32 or not R.is_contiguous():
-        raise ValueError("R must be contiguous float32 [d, d]")
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _want(t, nm, q.shape, torch.float32)
+    _want(R, "R", (d, d), torch.float32)
+    _same_gpu(q=q, k=k, v=v, R=R)
     nt = -(-N // FP8_TILE)
     codes = [torch.empty((B, H, N, d), dtype=torch.uint8, device=q.device) for _ in range(3)]
     scales = [torch.empty((B, H, nt), dtype=torch.float32, device=q.device) for _ in range(3)]
@@ -169,22 +203,25 @@ def attn_fp8_prepare(q, k, v, R, stream=None):
 def attn_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, scale=None, causal=False,
                  stream=None, with_lse=True):
     """Attention on e4m3 codes with per-tile scales; O is bf16."""
+    if q8.dim() != 4:
+        raise ValueError("q8, k8, v8 must be [B, H, N, d]")
     B, H, N, d = q8.shape
-    for t in (q8, k8, v8):
-        if t.shape != q8.shape or t.dtype != torch.uint8 or not t.is_contiguous():
-            raise ValueError("q8, k8, v8 must be contiguous uint8 [B, H, N, d]")
+    for nm, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _want(t, nm, q8.shape, torch.uint8)
     nt = -(-N // FP8_TILE)
-    for s in (sq, sk, sv):
-        if s.shape != (B, H, nt) or s.dtype != torch.float32 or not s.is_contiguous():
-            raise ValueError("scales must be contiguous float32 [B, H, ceil(N/128)]")
+    for nm, s_ in (("sq", sq), ("sk", sk), ("sv", sv)):
+        _want(s_, nm, (B, H, nt), torch.float32)
+    if o is not None:
+        _want(o, "o", (B, H, N, d), torch.bfloat16)
+    if lse is not None:
+        _want(lse, "lse", (B, H, N), torch.float32)
+    _same_gpu(q8=q8, k8=k8, v8=v8, sq=sq, sk=sk, sv=sv, o=o, lse=lse)
     if o is None:
         o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     st = lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv),
-                            _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+                            _ptr(o), _ptr(lse), B, H, N, d, _scale_arg(scale), int(bool(causal)),
                             _stream(stream))
     _check(st, "attn_fwd_fp8")
     return o, lse
@@ -198,27 +235,24 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, scale
     if q.dim() != 4:
         raise ValueError("q, k, v, o, dout must be [B, H, N, d]")
     B, H, N, d = q.shape
-    for t in (q, k, v, o, dout):
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v, o, dout must share shape, dtype and device")
-        if not t.is_contiguous():
-            raise ValueError("q, k, v, o, dout must be contiguous")
     if q.dtype != torch.bfloat16:
         raise ValueError("attn_bwd takes bfloat16 tensors")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    for nm, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _want(t, nm, q.shape, torch.bfloat16)
+    _want(lse, "lse", (B, H, N), torch.float32)
+    for nm, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _want(t, nm, q.shape, torch.bfloat16)
+    if delta is not None:
+        _want(delta, "delta", (B, H, N), torch.float32)
+    _same_gpu(q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    for t in (dq, dk, dv):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous bfloat16 like q")
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
-                        _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                        _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale_arg(scale),
                         int(bool(causal)), ATTN_BF16, _stream(stream))
     _check(st, "attn_bwd")
     return dq, dk, dv
@@ -226,12 +260,13 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, scale
 
 def attn_mxfp8_prepare(q, k, v, R, stream=None):
     """MXFP8 codes and E8M0 scale bytes ([B, H, N, d/32] uint8) of q R, k R and v."""
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, N, d = q.shape
-    for t in (q, k, v):
-        if t.shape != q.shape or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous float32 [B, H, N, d]")
-    if R.shape != (d, d) or R.dtype != torch.float32 or not R.is_contiguous():
-        raise ValueError("R must be contiguous float32 [d, d]")
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _want(t, nm, q.shape, torch.float32)
+    _want(R, "R", (d, d), torch.float32)
+    _same_gpu(q=q, k=k, v=v, R=R)
     codes = [torch.empty((B, H, N, d), dtype=torch.uint8, device=q.device) for _ in range(3)]
     scales = [torch.empty((B, H, N, d // MX_BLOCK), dtype=torch.uint8, device=q.device) for _ in range(3)]
     st = lib().attn_mxfp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(R), *(_ptr(c) for c in codes),
@@ -243,39 +278,42 @@ def attn_mxfp8_prepare(q, k, v, R, stream=None):
 def attn_fwd_mxfp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, scale=None, causal=False,
                    stream=None, with_lse=True):
     """Attention on MXFP8 codes with E8M0 block scales; O is bf16."""
+    if q8.dim() != 4:
+        raise ValueError("q8, k8, v8 must be [B, H, N, d]")
     B, H, N, d = q8.shape
-    for t in (q8, k8, v8):
-        if t.shape != q8.shape or t.dtype != torch.uint8 or not t.is_contiguous():
-            raise ValueError("q8, k8, v8 must be contiguous uint8 [B, H, N, d]")
-    for s_ in (sq, sk, sv):
-        if s_.shape != (B, H, N, d // MX_BLOCK) or s_.dtype != torch.uint8 or not s_.is_contiguous():
-            raise ValueError("scales must be contiguous uint8 [B, H, N, d/32]")
+    for nm, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _want(t, nm, q8.shape, torch.uint8)
+    for nm, s_ in (("sq", sq), ("sk", sk), ("sv", sv)):
+        _want(s_, nm, (B, H, N, d // MX_BLOCK), torch.uint8)
+    if o is not None:
+        _want(o, "o", (B, H, N, d), torch.bfloat16)
+    if lse is not None:
+        _want(lse, "lse", (B, H, N), torch.float32)
+    _same_gpu(q8=q8, k8=k8, v8=v8, sq=sq, sk=sk, sv=sv, o=o, lse=lse)
     if o is None:
         o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     st = lib().attn_fwd_mxfp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv),
-                              _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+                              _ptr(o), _ptr(lse), B, H, N, d, _scale_arg(scale), int(bool(causal)),
                               _stream(stream))
     _check(st, "attn_fwd_mxfp8")
     return o, lse
 
 
 def _w4_check(qweight, scales, zeros, K, group, device):
-    N = qweight.shape[0]
     if qweight.dim() != 2 or qweight.element_size() != 4 or qweight.dtype.is_floating_point:
         raise ValueError("qweight must be a 2-D tensor of 32-bit words [N, K/8]")
+    N = qweight.shape[0]
     if tuple(qweight.shape) != (N, K // 8):
         raise ValueError(f"qweight must be [N, K/8] = [{N}, {K // 8}]")
-    if scales.dtype != torch.float16 or tuple(scales.shape) != (N, K // group):
-        raise ValueError(f"scales must be float16 [N, K/{group}]")
-    if zeros.dtype != torch.uint8 or tuple(zeros.shape) != (N, K // group):
-        raise ValueError(f"zeros must be uint8 [N, K/{group}]")
-    for t in (qweight, scales, zeros):
-        if not t.is_contiguous() or t.device != device:
-            raise ValueError("qweight, scales, zeros must be contiguous and on the same device")
+    if not qweight.is_contiguous():
+        raise ValueError("qweight must be contiguous")
+    _want(scales, "scales", (N, K // group), torch.float16)
+    _want(zeros, "zeros", (N, K // group), torch.uint8)
+    for nm, t in (("qweight", qweight), ("scales", scales), ("zeros", zeros)):
+        if t.device != device:
+            raise ValueError(f"{nm} is on {t.device}, other arguments on {device}")
     return N
 
 
@@ -286,6 +324,9 @@ def w4a16_gemm(x, qweight, scales, zeros, y=None, group=W4A16_GROUP, stream=None
         raise ValueError("x must be a contiguous float16 [M, K] tensor")
     M, K = x.shape
     N = _w4_check(qweight, scales, zeros, K, group, x.device)
+    if y is not None:
+        _want(y, "y", (M, N), torch.float16)
+    _same_gpu(x=x, qweight=qweight, scales=scales, zeros=zeros, y=y)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     st = lib().w4a16_gemm(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), M, N, K,
@@ -297,6 +338,9 @@ def w4a16_gemm(x, qweight, scales, zeros, y=None, group=W4A16_GROUP, stream=None
 def w4a16_dequantize(qweight, scales, zeros, K, w=None, group=W4A16_GROUP, stream=None):
     """The fp16 weights [N, K] that w4a16_gemm feeds to the matrix cores."""
     N = _w4_check(qweight, scales, zeros, K, group, qweight.device)
+    if w is not None:
+        _want(w, "w", (N, K), torch.float16)
+    _same_gpu(qweight=qweight, scales=scales, zeros=zeros, w=w)
     if w is None:
         w = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
     st = lib().w4a16_dequantize(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(w), N, K,

@@ -25,8 +25,17 @@ int check_shape(int B, int H, int N, int d) {
   return ATTN_OK;
 }
 
-int check_scale(float scale) {
-  return (std::isfinite(scale) && scale > 0.f) ? ATTN_OK : ATTN_ERR_INVALID_ARG;
+// The softmax scale: finite and > 0 as given, or 0 for the scaled
+// dot-product's 1/sqrt(d) (page "Self-Attention, CUDA kernels and
+// FlashAttention", section 1).
+int resolve_scale(float scale, int d, float* out) {
+  if (scale == 0.f) {
+    *out = 1.f / std::sqrt(static_cast<float>(d));
+    return ATTN_OK;
+  }
+  if (!(std::isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  *out = scale;
+  return ATTN_OK;
 }
 
 int check_ptrs(const void* q, const void* k, const void* v, const void* o, const void* lse) {
@@ -43,7 +52,7 @@ int fwd_common(bool simple, const void* q, const void* k, const void* v, void* o
   int st = check_shape(B, H, N, d);
   if (st < 0) return st;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
-  if (check_scale(scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (resolve_scale(scale, d, &scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
   if (check_ptrs(q, k, v, o, lse) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
   if (st == 1) return ATTN_OK;
   attn127::LaunchArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, dtype, stream};
@@ -80,7 +89,7 @@ int fp8_fwd_common(bool mx, const uint8_t* q8, const uint8_t* k8, const uint8_t*
                    int B, int H, int N, int d, float scale, int causal, void* stream) {
   int st = check_shape(B, H, N, d);
   if (st < 0) return st;
-  if (check_scale(scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (resolve_scale(scale, d, &scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
   if (check_ptrs(q8, k8, v8, o, lse) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
   if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
   const void* ss[] = {q_scale, k_scale, v_scale};
@@ -158,7 +167,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (st < 0) return st;
   if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
-  if (check_scale(scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (resolve_scale(scale, d, &scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
   const void* ps[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : ps)
     if (!p || !aligned16(p)) return ATTN_ERR_INVALID_ARG;

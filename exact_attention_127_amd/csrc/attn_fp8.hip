@@ -11,12 +11,16 @@
 // attn_fwd_fp8: the bf16 kernel's structure (transposed scores, in-register
 // online softmax, deferred normalisation, HBM -> LDS copies) with the scores
 // on v_mfma_f32_32x32x64_f8f6f4: S^T = K^ Q^^T, the tile scales of Q and K
-// folded into the exponent's multiplier.  The second product stays on bf16
-// matrix cores: each wave converts the e4m3 V codes it copied into a bf16 V
-// tile (exact), and the V tile's scale rides on P (p * s_v rounded to bf16).
-// Rounding P to e4m3 instead would cost up to 2^-4 of every weight, which
-// with the x40 outlier channels of V exceeds the accuracy bound; bf16 P costs
-// 2^-9.
+// folded into the exponent's multiplier.  The second product runs on fp16
+// matrix cores: each wave converts the e4m3 V codes it copied into an fp16 V
+// tile (exact: every e4m3 value is an fp16 value), and the V tile's scale,
+// relative to the largest V tile scale of the head, rides on P:
+// p * s_v / s_vmax is rounded to fp16 (2^-11 of each weight; it stays below
+// 2^8, far inside fp16's range).  Rounding P to e4m3 instead would cost up
+// to 2^-4 of every weight and bf16 2^-9; where the x40 outlier channels of V
+// cancel in O, a 2^-9 weight error reaches 9% of |O| (measured on the fp8
+// workload against float64 attention on the dequantised codes), 2^-11 about
+// 1%.
 #include <math.h>
 
 #include "common.h"
@@ -85,8 +89,9 @@ __device__ __forceinline__ void issue_copy8(char* dst, const uint8_t* src, int k
   }
 }
 
-// The blocks of a V tile this wave copied: e4m3 codes -> bf16 (exact), into
-// the bf16 tile.  Lane i's 16 codes are channels 16c..16c+15 of one row.
+// The blocks of a V tile this wave copied: e4m3 codes -> bf16 or fp16
+// (exact), into the 16-bit tile.  Lane i's 16 codes are channels
+// 16c..16c+15 of one row.
 // Row and channel chunk (16 codes) that lane `lane` converts in block b.
 template <int D, int NW>
 __device__ __forceinline__ void convert_slot(int wave, int lane, int b, int& row, int& c) {
@@ -98,7 +103,9 @@ __device__ __forceinline__ void convert_slot(int wave, int lane, int b, int& row
 
 // vscale[b]: the power of two multiplying block b's codes (1 for per-tile
 // scales, whose factor rides on P; 2^e of the 32-channel block for MXFP8).
-template <int D, int NW>
+// F16: fp16 codes (per-tile scales), else bf16 (MXFP8, whose block scales
+// span bf16's exponent range).
+template <int D, int NW, bool F16>
 __device__ __forceinline__ void convert_v(char* dst16, const char* src8, int wave, int lane,
                                           const float (&vscale)[Cfg8<D, NW>::BPW]) {
   using C = Cfg8<D, NW>;
@@ -112,10 +119,17 @@ __device__ __forceinline__ void convert_v(char* dst16, const char* src8, int wav
     u32x4 lo, hi;
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], sc, false));
-      lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], sc, true));
-      hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], sc, false));
-      hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], sc, true));
+      if constexpr (F16) {
+        lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[w], sc, false));
+        lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[w], sc, true));
+        hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[w + 2], sc, false));
+        hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[w + 2], sc, true));
+      } else {
+        lo[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], sc, false));
+        lo[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], sc, true));
+        hi[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], sc, false));
+        hi[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w + 2], sc, true));
+      }
     }
     char* r16 = dst16 + row * C::ROWB16;
     *reinterpret_cast<u32x4*>(r16 + (((2 * c) ^ swz16<D>(row)) << 4)) = lo;
@@ -142,16 +156,17 @@ __device__ __forceinline__ uint32_t load_row_scales(__amdgpu_buffer_rsrc_t r, in
 }
 #endif
 
-// Scores on fp8 MFMA; P V on bf16 MFMA with V^ converted exactly to bf16 and
-// the V tile scale carried by P (p * s_v rounded to bf16: the same relative
-// rounding as the bf16 kernel's P, where e4m3 P would lose up to 2^-4 of
-// each weight).
+// Scores on fp8 MFMA; P V on fp16 MFMA with V^ converted exactly to fp16
+// and the V tile scale, relative to the head's largest V tile scale s_vmax,
+// carried by P (p * s_v / s_vmax rounded to fp16); O is the accumulated
+// product times s_vmax over the normaliser.
 //
 // MX = true (MXFP8): every token row carries one E8M0 scale per 32 channels.
 // The score MFMA applies the K and Q block scales itself (each lane's 32
 // codes are one block), V is widened to bf16 with its block scale (exact),
-// and P carries no scale.  Each lane loads the scale bytes it needs with the
-// tile copies, so they are covered by the same wait.
+// and P carries no scale; P V stays on bf16 matrix cores there, since the
+// widened values span bf16's exponent range.  Each lane loads the scale bytes
+// it needs with the tile copies, so they are covered by the same wait.
 template <int D, int NW, bool CAUSAL, bool MX>
 __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
@@ -273,9 +288,19 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
                      static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
     }
   }
+  // per-tile scales: the head's largest V tile scale (V values are kept in
+  // its units on the fp16 path; every lane of every wave computes the same)
+  float svmax = 1.f;
+  if constexpr (!MX) {
+    float mxs = 0.f;
+    for (int t = lane; t < ntq; t += 64) mxs = fmaxf(mxs, svh[t]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mxs = fmaxf(mxs, __shfl_xor(mxs, off));
+    svmax = mxs;
+  }
   wait_vmcnt<0>();
   widen(vsc);
-  convert_v<D, NW>(vring, vstage, wave, lane, vsc);     // this wave's own copied blocks
+  convert_v<D, NW, !MX>(vring, vstage, wave, lane, vsc);     // this wave's own copied blocks
   __syncthreads();
 
   f32x16 oacc[D / 32];
@@ -353,10 +378,10 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       }
-      // operand p' = p * s_v = exp2(s*ct - m + log2 s_v); the normaliser
-      // takes sum(p') / s_v
-      const float svt = MX ? 1.f : svh[kv0 / kTile8];
-      const float mref = ((m == -INFINITY) ? 0.f : m) - (MX ? 0.f : __log2f(svt));
+      // operand p' = p * s_v / s_vmax = exp2(s*ct - m + log2(s_v / s_vmax));
+      // the normaliser takes sum(p') * s_vmax / s_v
+      const float svr = MX ? 1.f : svh[kv0 / kTile8] / svmax;
+      const float mref = ((m == -INFINITY) ? 0.f : m) - (MX ? 0.f : __log2f(svr));
       uint32_t pw[4][4];
       float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -367,19 +392,24 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
           const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], ct, -mref));
           ls0 += p0;
           ls1 += p1;
-          pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+          pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = MX ? pack_bf16x2(p0, p1) : pack_f16x2(p0, p1);
         }
-      lsum += MX ? (ls0 + ls1) : (ls0 + ls1) / svt;
-      // ---- O^T += V^T P'^T (bf16) ----
+      lsum += MX ? (ls0 + ls1) : (ls0 + ls1) / svr;
+      // ---- O^T += V^T P'^T (fp16; bf16 for MXFP8) ----
 #pragma unroll
       for (int c16 = 0; c16 < 4; ++c16) {
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
+        const u32x4 pwv = u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]};
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const v4i16 lo = ds_read_tr16(vst + vbase16[db] + (c16 * 16) * C::ROWB16);
           const v4i16 hi = ds_read_tr16(vst + vbase16[db] + (c16 * 16 + 8) * C::ROWB16);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+          const v8i16 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          if constexpr (MX)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                               __builtin_bit_cast(bf16x8, pwv), oacc[db], 0, 0, 0);
+          else
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                              __builtin_bit_cast(f16x8, pwv), oacc[db], 0, 0, 0);
         }
       }
     }
@@ -389,7 +419,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
       // previous barrier)
       wait_vmcnt<0>();
       widen(vsc);
-      convert_v<D, NW>(vring + ((t + 1) & 1) * C::TILEB16, vstage, wave, lane, vsc);
+      convert_v<D, NW, !MX>(vring + ((t + 1) & 1) * C::TILEB16, vstage, wave, lane, vsc);
       kscw[0] = kscw_next[0];
       kscw[1] = kscw_next[1];
     }
@@ -398,7 +428,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
 
   const float ltot = halves_sum(lsum);
   if (qrow < N) {
-    const float inv = 1.f / ltot;
+    const float inv = svmax / ltot;
     uint16_t* orow = o + base + static_cast<int64_t>(qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

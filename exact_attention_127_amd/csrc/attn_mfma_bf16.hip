@@ -207,62 +207,75 @@ __device__ __forceinline__ float tile_max(const f32x16 (&sacc)[BC / 32]) {
   return mx;
 }
 
-// p = exp2(t) for pair pr of a tile: the float32 p go into the normaliser,
-// the bf16-rounded p into the B operand of P V (accumulator registers
+// A tile's 16 score pairs per lane form 4 P operands of 4 packed words each
+// (pair pr -> word pr%4 of operand pr/4).  The last operand of tile t+1 (its
+// "early" pairs, keys 48..63) is formed in the P V phase of tile t, right
+// after that tile's exponents are known; the other pairs ("late") follow in
+// the score phase of tile t+1.  This moves a quarter of the exponential work
+// to the phase whose vector pipe is otherwise less loaded (measured on an
+// instruction-level model of the tile: 1096 -> 1022 ns; moving 3, 5, 6 or 7
+// pairs instead measured slower in the kernel).
+constexpr int kOps = BC / 16;                           // P operands per tile
+constexpr int kPairs = BC / 4;                          // score pairs per lane and tile
+constexpr int kEarly = 4;                               // pairs formed early
+constexpr int kLate = kPairs - kEarly;                  // pairs formed in the score phase
+constexpr int kEarlyP0 = kLate;                         // first early pair
+
+// k-th early pair / k-th late pair of a tile, and whether a pair is early
+__device__ __forceinline__ constexpr int early_pair(int k) { return kEarlyP0 + k; }
+__device__ __forceinline__ constexpr int late_pair(int k) { return k; }
+__device__ __forceinline__ constexpr bool is_early(int pr) { return pr >= kEarlyP0; }
+
+// Packed bf16 numerators of a tile: the early words (formed one phase ahead)
+// and the late words (indexed by pair; only late pairs are used).
+struct EarlyWords {
+  uint32_t w[kEarly];
+};
+struct LateWords {
+  uint32_t w[kPairs];
+};
+
+// p = exp2(t) for pair pr of a tile (two keys of the lane's query: scores
+// r and r+1 of key block kb).  The float32 p go into the normaliser, the
+// bf16-rounded p into the pair's packed word (accumulator registers
 // 8c'..8c'+7 of key block kb form operand 2kb+c').
-__device__ __forceinline__ void exp_pair(uint32_t (&pw)[BC / 16][4], float& ls0, float& ls1,
-                                         const f32x16 (&t)[BC / 32], int pr) {
+__device__ __forceinline__ void exp2_pair(float& p0, float& p1, const f32x16 (&t)[BC / 32], int pr) {
   const int kb = pr / 8, r = (pr % 8) * 2;
-  const float p0 = fast_exp2(t[kb][r]);
-  const float p1 = fast_exp2(t[kb][r + 1]);
+  p0 = fast_exp2(t[kb][r]);
+  p1 = fast_exp2(t[kb][r + 1]);
+}
+__device__ __forceinline__ void sum_pack(uint32_t& word, float& ls0, float& ls1, float p0, float p1) {
   ls0 += p0;
   ls1 += p1;
-  pw[kb * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+  word = pack_bf16x2(p0, p1);
 }
-
-// The last P operand of a tile (its last 16 keys: score pairs kFirstEarly..
-// of the second key block) is formed one phase early, in the P V phase of
-// the previous tile, right after that tile's exponents are known; the rest
-// follows in the score phase.  This moves a quarter of the exponential work
-// to the phase whose vector pipe is otherwise half idle (measured on an
-// instruction-level model of the tile: 1096 -> 1022 ns).
-constexpr int kEarly = 4;                       // pairs formed early
-constexpr int kFirstEarly = BC / 4 - kEarly;    // = 12
-constexpr int kLateOps = BC / 16 - 1;           // P operands formed in the score phase
-static_assert(kEarly * 4 == 16 && kFirstEarly % 8 == 4, "early pairs fill the last operand");
-
-__device__ __forceinline__ void exp_early(uint32_t (&pw)[4], float& l0, float& l1,
-                                          const f32x16 (&t)[BC / 32], int k) {
-  const int r = ((kFirstEarly + k) % 8) * 2;     // key block BC/32 - 1
-  const float p0 = fast_exp2(t[BC / 32 - 1][r]);
-  const float p1 = fast_exp2(t[BC / 32 - 1][r + 1]);
-  l0 += p0;
-  l1 += p1;
-  pw[k] = pack_bf16x2(p0, p1);
+__device__ __forceinline__ void exp_pair(uint32_t& word, float& ls0, float& ls1, const f32x16 (&t)[BC / 32],
+                                         int pr) {
+  float p0, p1;
+  exp2_pair(p0, p1, t, pr);
+  sum_pack(word, ls0, ls1, p0, p1);
 }
 
 // All early pairs of a tile at once (first tile, and after a reference shift).
-__device__ __forceinline__ void early_operand(bf16x8& pe, float& le, const f32x16 (&t)[BC / 32]) {
-  uint32_t pw[4];
+__device__ __forceinline__ void early_words(EarlyWords& pe, float& le, const f32x16 (&t)[BC / 32]) {
   float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-  for (int k = 0; k < kEarly; ++k) exp_early(pw, l0, l1, t, k);
-  pe = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+  for (int k = 0; k < kEarly; ++k) exp_pair(pe.w[k], l0, l1, t, early_pair(k));
   le = l0 + l1;
 }
 
 // First tile: the exponent reference becomes the row's scaled maximum, the
-// scores become exponents t = s*c - m in place, and the early operand forms.
+// scores become exponents t = s*c - m in place, and the early words form.
 template <int D>
 __device__ __forceinline__ void first_reference(WaveState<D>& w, f32x16 (&s)[BC / 32], float c,
-                                                bf16x8& pe, float& le) {
+                                                EarlyWords& pe, float& le) {
   w.m = halves_max(tile_max(s)) * c;
   const float mref = (w.m == -INFINITY) ? 0.f : w.m;
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -mref);
-  early_operand(pe, le, s);
+  early_words(pe, le, s);
 }
 
 // Later tiles arrive as exponents t = s*c - m against the current reference
@@ -282,30 +295,20 @@ __device__ __forceinline__ bool tile_overflows(float lsum_tile) {
   return __builtin_amdgcn_ballot_w64(!(lsum_tile <= kGuard)) != 0;
 }
 
-template <int D>
-__device__ __forceinline__ void pack_operands(bf16x8 (&pb)[kLateOps], const uint32_t (&pw)[BC / 16][4]) {
-#pragma unroll
-  for (int c16 = 0; c16 < kLateOps; ++c16)
-    pb[c16] = __builtin_bit_cast(bf16x8, u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]});
-}
-
 // Numerators of a tile's late pairs at once (the last tile, which is not
 // pipelined, and the overflow path); ll receives their sum.
-template <int D>
-__device__ __forceinline__ void late_operands(bf16x8 (&pb)[kLateOps], float& ll, const f32x16 (&t)[BC / 32]) {
-  uint32_t pw[BC / 16][4];
+__device__ __forceinline__ void late_words(LateWords& pl, float& ll, const f32x16 (&t)[BC / 32]) {
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-  for (int pr = 0; pr < kFirstEarly; ++pr) exp_pair(pw, ls0, ls1, t, pr);
+  for (int j = 0; j < kLate; ++j) exp_pair(pl.w[late_pair(j)], ls0, ls1, t, late_pair(j));
   ll = ls0 + ls1;
-  pack_operands<D>(pb, pw);
 }
 
 // Overflow path: the tile's exact maximum exponent becomes the reference
 // (rows whose maximum is not above it keep theirs).
 template <int D>
-__device__ __forceinline__ void rebase_tile(WaveState<D>& w, f32x16 (&t)[BC / 32], bf16x8 (&pb)[kLateOps],
-                                            bf16x8& pe, float& le, float& ll) {
+__device__ __forceinline__ void rebase_tile(WaveState<D>& w, f32x16 (&t)[BC / 32], LateWords& pl,
+                                            EarlyWords& pe, float& le, float& ll) {
   const float delta = fmaxf(halves_max(tile_max(t)), 0.f);
   const float alpha = fast_exp2(-delta);
   w.lsum *= alpha;
@@ -316,31 +319,35 @@ __device__ __forceinline__ void rebase_tile(WaveState<D>& w, f32x16 (&t)[BC / 32
   for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) t[kb][r] -= delta;
-  early_operand(pe, le, t);
-  late_operands<D>(pb, ll, t);
+  early_words(pe, le, t);
+  late_words(pl, ll, t);
 }
 
 // The guard and the normaliser update of a tile whose numerators are formed.
 template <int D>
-__device__ __forceinline__ void commit_tile(WaveState<D>& w, f32x16 (&t)[BC / 32], bf16x8 (&pb)[kLateOps],
-                                            bf16x8& pe, float& le, float ll) {
-  if (tile_overflows<D>(ll + le)) rebase_tile<D>(w, t, pb, pe, le, ll);
+__device__ __forceinline__ void commit_tile(WaveState<D>& w, f32x16 (&t)[BC / 32], LateWords& pl,
+                                            EarlyWords& pe, float& le, float ll) {
+  if (tile_overflows<D>(ll + le)) rebase_tile<D>(w, t, pl, pe, le, ll);
   w.lsum += ll + le;
 }
 
-template <int D>
-__device__ __forceinline__ const bf16x8& p_operand(const bf16x8 (&pb)[kLateOps], const bf16x8& pe, int c16) {
-  return c16 < kLateOps ? pb[c16] : pe;
+// P operand c16 of a tile: its four packed words, early or late.
+__device__ __forceinline__ uint32_t p_word(const LateWords& pl, const EarlyWords& pe, int pr) {
+  return is_early(pr) ? pe.w[pr - kEarlyP0] : pl.w[pr];
+}
+__device__ __forceinline__ bf16x8 p_operand(const LateWords& pl, const EarlyWords& pe, int c16) {
+  return __builtin_bit_cast(bf16x8, u32x4{p_word(pl, pe, 4 * c16), p_word(pl, pe, 4 * c16 + 1),
+                                          p_word(pl, pe, 4 * c16 + 2), p_word(pl, pe, 4 * c16 + 3)});
 }
 
 // O^T += V^T P^T for one tile, V^T through transposing LDS reads.
 template <int D>
-__device__ __forceinline__ void pv_tile(WaveState<D>& w, const bf16x8 (&pb)[kLateOps], const bf16x8& pe,
+__device__ __forceinline__ void pv_tile(WaveState<D>& w, const LateWords& pl, const EarlyWords& pe,
                                         const LaneAddr<D>& la, const char* vst) {
 #pragma unroll
   for (int i = 0; i < Ops<D>::NM; ++i) {
     const int db = i / (BC / 16), c16 = i % (BC / 16);
-    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vst, la, i), p_operand<D>(pb, pe, c16),
+    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vst, la, i), p_operand(pl, pe, c16),
                                                          w.oacc[db], 0, 0, 0);
   }
 }
@@ -361,15 +368,18 @@ constexpr int kReadAheadK = 3;   // score operands in flight
 constexpr int kReadAheadV = 2;   // output operands in flight (two reads each)
 
 // Phase A: scores of the next tile on the matrix cores beside the
-// exponentials, normaliser and bf16 packing of the current tile's first
-// kFirstEarly pairs (spread evenly over the slots).
+// exponentials, normaliser and bf16 packing of the current tile's late
+// pairs (spread evenly over the slots).  A pair's normaliser sum and bf16
+// pack run one slot after its exponentials, so they never wait on the
+// transcendental unit's result (measured: 0.909 -> 0.889 ms at N=16384,
+// identical results).
 template <int D>
-__device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32],
-                                        bf16x8 (&pb)[kLateOps], float& ll, const f32x16 (&tcur)[BC / 32],
-                                        const LaneAddr<D>& la, const char* kst_next) {
+__device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32], LateWords& pl, float& ll,
+                                        const f32x16 (&tcur)[BC / 32], const LaneAddr<D>& la,
+                                        const char* kst_next) {
   constexpr int NM = Ops<D>::NM, KA = kReadAheadK;
   bf16x8 kop[NM];
-  uint32_t pw[BC / 16][4];
+  float pp[kLate][2];
   float ls0 = 0.f, ls1 = 0.f;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -381,33 +391,43 @@ __device__ __forceinline__ void phase_a(WaveState<D>& w, f32x16 (&snext)[BC / 32
     snext[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], w.qr[ks],
                                                         ks == 0 ? f32x16{} : snext[kb], 0, 0, 0);
 #pragma unroll
-    for (int pr = 0; pr < kFirstEarly; ++pr) {
-      if ((pr * NM) / kFirstEarly != i) continue;
-      const int kb2 = pr / 8, r = (pr % 8) * 2;
-      exp_pair(pw, ls0, ls1, tcur, pr);
-      pin(pw[kb2 * 2 + (r >> 3)][(r & 7) >> 1]);
+    for (int j = 0; j < kLate; ++j) {
+      const int pr = late_pair(j), sl = (j * NM) / kLate;
+      if (sl == i - 1) {
+        sum_pack(pl.w[pr], ls0, ls1, pp[j][0], pp[j][1]);
+        pin(pl.w[pr]);
+      }
+      if (sl == i) {
+        exp2_pair(pp[j][0], pp[j][1], tcur, pr);
+        pin(pp[j][0]);
+        pin(pp[j][1]);
+      }
     }
     pin(ls0);
     pin(ls1);
     __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int j = 0; j < kLate; ++j) {
+    const int pr = late_pair(j);
+    if ((j * NM) / kLate == NM - 1) sum_pack(pl.w[pr], ls0, ls1, pp[j][0], pp[j][1]);
+  }
   ll = ls0 + ls1;
-  pack_operands<D>(pb, pw);
 }
 
 // Phase B: P V of the current tile on the matrix cores beside the scaling
 // (t = s*c - m) of the next tile, whose masked keys (causal diagonal,
 // sequence end) were set to -inf before the phase, and the next tile's
-// early operand.  The early pairs are scaled first.
+// early pairs.  The early pairs are scaled first.
 template <int D>
-__device__ __forceinline__ void phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32],
-                                         const bf16x8 (&pb)[kLateOps], const bf16x8& pecur,
-                                         bf16x8& penext, float& lenext, const LaneAddr<D>& la,
-                                         const char* vst, float c) {
+__device__ __forceinline__ void phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32], const LateWords& pl,
+                                         const EarlyWords& pecur, EarlyWords& penext, float& lenext,
+                                         const LaneAddr<D>& la, const char* vst, float c) {
   constexpr int NM = Ops<D>::NM, PPS = Ops<D>::PPS, VA = kReadAheadV;
-  constexpr int S0 = kEarly / PPS;               // slots that scale the early pairs
+  constexpr int S0 = (kEarly + PPS - 1) / PPS;   // slots that scale the early pairs
+  static_assert(S0 < NM, "early pairs leave slots for their exponentials");
   bf16x8 vop[NM];
-  uint32_t pw[4];
+  float pp[kEarly][2];
   float l0 = 0.f, l1 = 0.f;
   const float mref = w.m;
   __builtin_amdgcn_sched_barrier(0);
@@ -417,10 +437,13 @@ __device__ __forceinline__ void phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32
   for (int i = 0; i < NM; ++i) {
     if (i + VA < NM) vop[i + VA] = v_operand<D>(vst, la, i + VA);
     const int db = i / (BC / 16), c16 = i % (BC / 16);
-    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], p_operand<D>(pb, pecur, c16), w.oacc[db], 0, 0, 0);
+    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], p_operand(pl, pecur, c16), w.oacc[db], 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < PPS; ++u) {
-      const int pr = (i * PPS + u + kFirstEarly) % Ops<D>::PAIRS, kb = pr / 8, r = (pr % 8) * 2;
+      // scaling order: the early pairs, then the late ones
+      const int q = i * PPS + u;
+      const int pr = q < kEarly ? early_pair(q) : late_pair(q - kEarly);
+      const int kb = pr / 8, r = (pr % 8) * 2;
       snext[kb][r] = fmaf(snext[kb][r], c, -mref);           // -inf stays -inf (c > 0)
       snext[kb][r + 1] = fmaf(snext[kb][r + 1], c, -mref);
       pin(snext[kb][r]);
@@ -428,15 +451,26 @@ __device__ __forceinline__ void phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32
     }
 #pragma unroll
     for (int k = 0; k < kEarly; ++k) {
-      if (S0 + (k * (NM - S0)) / kEarly != i) continue;
-      exp_early(pw, l0, l1, snext, k);
-      pin(pw[k]);
-      pin(l0);
-      pin(l1);
+      const int pr = early_pair(k);
+      const int sl = S0 + (k * (NM - S0)) / kEarly;
+      if (sl == i - 1) {
+        sum_pack(penext.w[k], l0, l1, pp[k][0], pp[k][1]);
+        pin(penext.w[k]);
+        pin(l0);
+        pin(l1);
+      }
+      if (sl == i) {
+        exp2_pair(pp[k][0], pp[k][1], snext, pr);
+        pin(pp[k][0]);
+        pin(pp[k][1]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  penext = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+  for (int k = 0; k < kEarly; ++k) {
+    if (S0 + (k * (NM - S0)) / kEarly == NM - 1) sum_pack(penext.w[k], l0, l1, pp[k][0], pp[k][1]);
+  }
   lenext = l0 + l1;
 }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -523,9 +557,9 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __syncthreads();
 
   f32x16 sa[BC / 32], sb[BC / 32];   // scores of the current and the next tile
-  bf16x8 pea, peb;                   // their early P operands ...
+  EarlyWords pea, peb;               // their early numerators ...
   float lea = 0.f, leb = 0.f;        // ... and those operands' normaliser shares
-  bf16x8 pb[kLateOps];
+  LateWords pb;
   if (last >= 0) {
     scores<D>(sa, w, la, kring);
     if ((causal && BC - 1 > q0w) || BC > N) apply_mask(sa, 0, N, qrow, h, causal);
@@ -538,8 +572,8 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // in LDS.  Iteration t copies V of t+1 and K of t+2.
   // The score buffers alternate roles each tile; two tiles per trip keep
   // that choice static.
-  auto iteration = [&](int t, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32], bf16x8& pecur,
-                       bf16x8& penext, float& lecur, float& lenext) {
+  auto iteration = [&](int t, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32], EarlyWords& pecur,
+                       EarlyWords& penext, float& lecur, float& lenext) {
     const char* kst_next = kring + ((t + 1) & 1) * C::TILEB;
     const char* vst = vring + (t & 1) * C::TILEB;
     if (t + 1 < ntiles) issue_copy<D, NW, true>(vring_a + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave, lane);
@@ -554,7 +588,7 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       phase_b<D>(w, snext, pb, pecur, penext, lenext, la, vst, c);
     } else if (t == last) {
       float ll;
-      late_operands<D>(pb, ll, scur);
+      late_words(pb, ll, scur);
       commit_tile<D>(w, scur, pb, pecur, lecur, ll);
       pv_tile<D>(w, pb, pecur, la, vst);
     }

@@ -8,6 +8,8 @@ namespace attn127 {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -28,6 +30,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// float -> fp16 bit pattern, round to nearest, ties to even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  f16x2 b = __builtin_convertvector(v, f16x2);
   return __builtin_bit_cast(uint32_t, b);
 }
 

@@ -21,7 +21,9 @@
  *              Element (b,h,i,c) sits at ((b*H + h)*N + i)*d + c.
  *   Causal     causal != 0 masks key j for query i when j > i (square
  *              self-attention: row i sees keys 0..i).
- *   Scale      scale must be finite and > 0 (the pages use 1/sqrt(d)).
+ *   Scale      scale must be finite and > 0, or exactly 0 to select
+ *              1/sqrt(d), the scaled dot-product's own factor (page
+ *              "Self-Attention, CUDA kernels and FlashAttention", section 1).
  *   Sizes      B, H, N >= 0 (any zero makes the call a no-op that returns
  *              ATTN_OK); d must be 64 or 128; B*H*N*d < 2^31 is not needed
  *              (offsets are 64-bit), but B*H < 2^31 and N < 2^30.
@@ -115,7 +117,10 @@ int attn_fp8_prepare(const float* q, const float* k, const float* v,
                      int B, int H, int N, int d, void* stream);
 
 /*
- * attn_fwd_fp8 -- attention on the e4m3 tensors attn_fp8_prepare writes.
+ * attn_fwd_fp8 -- attention on the e4m3 tensors attn_fp8_prepare writes
+ * (page "FlashAttention scaling, multi-GPU training and weight
+ * quantization", section 1, the FP8 bullet: the score product on FP8 matrix
+ * units, inputs block-quantised with one scale per tile).
  * Value of an input element = decode(code) * scale of its 128-token tile.
  * Q K^T runs on fp8 MFMA (e4m3 x e4m3, float32 accumulation) with the Q and
  * K tile scales folded into the exponent's multiplier.  P V runs on bf16
@@ -189,7 +194,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              void* dk, void* dv, int B, int H, int N, int d, float scale,
              int causal, int dtype, void* stream);
 
-/* Static, human-readable text for a status code (never NULL). */
 /* Weights per scale group of the W4A16 product. */
 #define W4A16_GROUP 128
 
@@ -229,6 +233,7 @@ int w4a16_dequantize(const uint32_t* qweight, const void* scales,
                      const uint8_t* zeros, void* w, int N, int K, int group,
                      void* stream);
 
+/* Static, human-readable text for a status code (never NULL). */
 const char* attn_strerror(int status);
 
 #ifdef __cplusplus

@@ -37,7 +37,7 @@ central finite differences of the forward oracle and against invariants (the
 dK rows sum to zero, the dV rows sum to the dO rows, identical keys give
 dQ = 0).  Every function here is pinned; none is "parity unpinned".
 """
-from .exact import attention, attention_rows, attention_probs, lse_rows
+from .exact import attention, attention_rows, attention_probs
 from .formats import (bf16_round, bf16_half_ulp, fp16_round, e4m3_decode, e4m3_encode,
                       E4M3_MAX, e4m3_table)
 from .fp8 import fp8_prepare, fp8_dequantize, QUANT_TILE
@@ -46,7 +46,7 @@ from .backward import (attention_backward, attention_backward_head, row_delta,
 from .mx import mxfp8_prepare, quantize_mx, dequantize_mx, mx_exponent, MX_BLOCK
 from .w4a16 import unpack_int4, pack_int4, dequantize, w4a16_gemm, w4a16_rows, w4a16_sum_abs
 
-__all__ = ["attention", "attention_rows", "attention_probs", "lse_rows",
+__all__ = ["attention", "attention_rows", "attention_probs",
            "bf16_round", "bf16_half_ulp", "e4m3_decode", "e4m3_encode",
            "E4M3_MAX", "e4m3_table", "fp8_prepare", "fp8_dequantize",
            "QUANT_TILE", "attention_backward", "attention_backward_head",

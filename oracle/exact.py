@@ -92,15 +92,6 @@ def attention(q, k, v, scale, causal):
     return o, lse
 
 
-def lse_rows(q, k, scale, causal, rows):
-    """LSE only, for the selected rows of one head."""
-    q64 = np.asarray(q, dtype=np.float64)
-    k64 = np.asarray(k, dtype=np.float64)
-    rows = np.asarray(rows, dtype=np.int64)
-    s = _scores(q64, k64, rows, scale, causal)
-    return _softmax_stats(s)[1]
-
-
 def attention_probs(q, k, scale, causal):
     """The full probability matrix P of one head (small inputs only)."""
     q64 = np.asarray(q, dtype=np.float64)

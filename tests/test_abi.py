@@ -49,7 +49,7 @@ def _fwd(fn, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=1, N=8, d=64, scal
     dict(q=None), dict(k=None), dict(v=None), dict(o=None),
     dict(q=FAKE + 2), dict(o=FAKE + 8), dict(lse=FAKE + 2),
     dict(d=32), dict(d=96), dict(d=0), dict(N=-1), dict(B=-1), dict(H=-2),
-    dict(dtype=2), dict(dtype=-1), dict(scale=0.0), dict(scale=-1.0),
+    dict(dtype=2), dict(dtype=-1), dict(scale=-1.0),
     dict(scale=float("inf")), dict(scale=float("nan")), dict(N=1 << 30),
 ])
 def test_invalid_arguments_rejected(fn, bad):
@@ -90,7 +90,7 @@ def _bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, delta=FAKE, dq=FAKE,
     dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(do=None), dict(lse=None),
     dict(delta=None), dict(dq=None), dict(dk=None), dict(dv=None),
     dict(do=FAKE + 8), dict(dq=FAKE + 2), dict(lse=FAKE + 2), dict(delta=FAKE + 1),
-    dict(d=96), dict(N=-1), dict(dtype=2), dict(scale=0.0), dict(scale=float("nan")),
+    dict(d=96), dict(N=-1), dict(dtype=2), dict(scale=-0.5), dict(scale=float("nan")),
 ])
 def test_bwd_invalid_arguments_rejected(bad):
     assert _bwd(**bad) == -1
@@ -137,3 +137,94 @@ def test_w4a16_entry_points_validate():
         L.w4a16_dequantize(q, s, z, w, N, K, group, None)
     assert d(w=FAKE + 8) == -1 and d(K=120) == -1 and d(group=32) == -2
     assert d(N=0) == 0
+
+
+# --- the Python binding checks every tensor before any pointer reaches the ABI
+
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = _t(1, 2, 8, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_fwd(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_fwd_simple(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_bwd(q, q, q, q, q, _t(1, 2, 8, dtype=torch.float32))
+    f = _t(1, 2, 8, 64, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_fp8_prepare(f, f, f, _t(64, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_mxfp8_prepare(f, f, f, _t(64, 64, dtype=torch.float32))
+    c = _t(1, 2, 8, 64, dtype=torch.uint8)
+    s = _t(1, 2, 1, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_fwd_fp8(c, c, c, s, s, s)
+    e = _t(1, 2, 8, 2, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_fwd_mxfp8(c, c, c, e, e, e)
+    x = _t(1, 256, dtype=torch.float16)
+    qw = _t(32, 32, dtype=torch.int32)
+    sc = _t(32, 2, dtype=torch.float16)
+    z = _t(32, 2, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        A.w4a16_gemm(x, qw, sc, z)
+    with pytest.raises(ValueError, match="GPU"):
+        A.w4a16_dequantize(qw, sc, z, 256)
+
+
+@pytest.mark.parametrize("bad", ["o_shape", "o_dtype", "o_strided", "lse_shape", "lse_dtype",
+                                 "k_shape", "v_dtype"])
+def test_binding_rejects_mismatched_outputs(bad):
+    import torch
+    q = _t(1, 2, 8, 64)
+    k, v = q.clone(), q.clone()
+    o = _t(1, 2, 8, 64)
+    lse = _t(1, 2, 8, dtype=torch.float32)
+    if bad == "o_shape":
+        o = _t(1, 2, 7, 64)
+    elif bad == "o_dtype":
+        o = _t(1, 2, 8, 64, dtype=torch.float32)
+    elif bad == "o_strided":
+        o = _t(1, 2, 64, 8).transpose(2, 3)
+    elif bad == "lse_shape":
+        lse = _t(1, 2, 4, dtype=torch.float32)
+    elif bad == "lse_dtype":
+        lse = _t(1, 2, 8)
+    elif bad == "k_shape":
+        k = _t(1, 2, 9, 64)
+    elif bad == "v_dtype":
+        v = _t(1, 2, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        A.attn_fwd(q, k, v, o=o, lse=lse)
+
+
+def test_binding_rejects_mismatched_scratch_and_gradients():
+    import torch
+    q = _t(1, 2, 8, 64)
+    lse = _t(1, 2, 8, dtype=torch.float32)
+    with pytest.raises(ValueError, match="delta"):
+        A.attn_bwd(q, q, q, q, q, lse, delta=_t(1, 2, 7, dtype=torch.float32))
+    with pytest.raises(ValueError, match="dq"):
+        A.attn_bwd(q, q, q, q, q, lse, dq=_t(1, 2, 8, 128))
+    with pytest.raises(ValueError, match="lse"):
+        A.attn_bwd(q, q, q, q, q, _t(1, 2, 8))
+    c = _t(1, 2, 8, 64, dtype=torch.uint8)
+    s = _t(1, 2, 1, dtype=torch.float32)
+    with pytest.raises(ValueError, match="sk"):
+        A.attn_fwd_fp8(c, c, c, s, _t(1, 2, 2, dtype=torch.float32), s)
+    with pytest.raises(ValueError, match="o"):
+        A.attn_fwd_fp8(c, c, c, s, s, s, o=_t(1, 2, 8, 64, dtype=torch.float32))
+    x = _t(2, 256, dtype=torch.float16)
+    qw = _t(32, 32, dtype=torch.int32)
+    sc = _t(32, 2, dtype=torch.float16)
+    z = _t(32, 2, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="y"):
+        A.w4a16_gemm(x, qw, sc, z, y=_t(1, 32, dtype=torch.float16))
+    with pytest.raises(ValueError, match="scales"):
+        A.w4a16_gemm(x, qw, _t(32, 3, dtype=torch.float16), z)

@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import to_device
+from helpers import oracle_bwd_heads, to_device
 from seeded_inputs import WORKLOADS, make_inputs, make_output_grad, random_inputs
 
 pytestmark = pytest.mark.gpu
@@ -96,6 +96,42 @@ def test_backward_is_deterministic(gpu):
     b = _run(inp, do, gpu)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# B*H = 128 causal with per-head Q/dO (dQ kernel) and K/V (dK/dV kernel)
+# bytes above 1 MiB: each XCD walks its 16 heads in two chunks of 8; every
+# element of every gradient is compared
+def test_two_head_chunks_per_xcd(gpu):
+    inp = random_inputs(16, 8, 2112, 128, "bf16", True, seed=510)
+    do = make_output_grad(inp["workload"])
+    dq, dk, dv = _run(inp, do, gpu)
+    heads = [(b, h) for b in range(16) for h in range(8)]
+    rq, rk, rv = oracle_bwd_heads(inp, do, heads)
+    _check("two chunks dq", dq.reshape(rq.shape), rq, REL_MAX_LONG, REL_MEAN_LONG)
+    _check("two chunks dk", dk.reshape(rk.shape), rk, REL_MAX_LONG, REL_MEAN_LONG)
+    _check("two chunks dv", dv.reshape(rv.shape), rv, REL_MAX_LONG, REL_MEAN_LONG)
+
+
+def test_guard_bands_untouched(gpu):
+    """attn_bwd writes dQ, dK, dV and D and nothing around them."""
+    import torch
+    import exact_attention_127_amd as A
+    B, H, N, d = 1, 3, 777, 128
+    inp = random_inputs(B, H, N, d, "bf16", True, seed=12)
+    do_np = make_output_grad(inp["workload"])
+    q, k, v, do = (to_device(x, torch.bfloat16, gpu) for x in (inp["q"], inp["k"], inp["v"], do_np))
+    o, lse = A.attn_fwd(q, k, v, scale=inp["scale"], causal=True)
+    G, n, m = 4096, B * H * N * d, B * H * N
+    bigs = [torch.full((n + 2 * G,), 7.0, dtype=torch.bfloat16, device=gpu) for _ in range(3)]
+    dbig = torch.full((m + 2 * G,), 7.0, dtype=torch.float32, device=gpu)
+    dq, dk, dv = (x[G:G + n].view(B, H, N, d) for x in bigs)
+    delta = dbig[G:G + m].view(B, H, N)
+    A.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, delta=delta, scale=inp["scale"], causal=True)
+    torch.cuda.synchronize()
+    for x in bigs:
+        assert (x[:G] == 7).all() and (x[G + n:] == 7).all()
+    assert (dbig[:G] == 7).all() and (dbig[G + m:] == 7).all()
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
 
 
 def _sampled(inp, do, dev_grads, heads, rows, cols):

@@ -9,9 +9,12 @@
   dequantised inputs the kernel consumes (codes made by the oracle) -- under
   |O - O_B| <= 6e-2 * max(1, |O_B|) (6e-2 ~ 2^-4, e4m3's relative spacing,
   taken as relative once |O| > 1), and, for the fp8 workload without
-  outliers, with the unquantised oracle under max-abs <= 6e-2.  The literal
-  outlier workload against the unquantised oracle is printed, not gated:
-  input quantisation of the x40 channels alone moves O far beyond 6e-2.
+  outliers, with the unquantised oracle under max-abs <= 6e-2 (gate G1).
+  The literal outlier workload is gated against oracle B (gate G2) on 8 heads
+  at every row; against the unquantised oracle its literal 6e-2 gate fails,
+  recorded as a strict expected failure with the measured value beside the
+  input-quantisation floor |O_B - O_A|: quantising the x40 channels alone
+  moves O far beyond 6e-2.
 """
 import numpy as np
 import pytest
@@ -19,6 +22,7 @@ import pytest
 import exact_attention_127_amd as A
 import oracle
 from seeded_inputs import WORKLOADS, haar_orthogonal, make_inputs, random_inputs
+from tests.helpers import oracle_heads, record_parity
 
 pytestmark = pytest.mark.gpu
 TOL8 = 6e-2
@@ -167,67 +171,138 @@ def test_fwd_fp8_head_grouped_grid(gpu, d, causal):
 
 
 def _sample_heads(w, n, seed):
+    """n distinct (b, h) pairs, always including the first and the last head."""
     rng = np.random.default_rng(seed)
-    return sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(n)} | {(0, 0)})
+    heads = {(0, 0), (w.B - 1, w.H - 1)}
+    while len(heads) < n:
+        heads.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    return sorted(heads)
+
+
+def _full_pipeline(inp, gpu):
+    """attn_fp8_prepare + attn_fwd_fp8 on the GPU over the whole workload."""
+    import torch
+    w = inp["workload"]
+    q8, k8, v8, sq, sk, sv = A.attn_fp8_prepare(*(_dev(inp[x], gpu) for x in "qkv"), _dev(inp["R"], gpu))
+    o, lse = A.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
 def test_fp8_workload_no_outliers_vs_unquantised(gpu):
     """Gate G1: the fp8 workload's shapes, rotation and tile scales without the
-    outlier channels, full pipeline on the GPU, against the unquantised oracle."""
+    outlier channels, full pipeline on the GPU, against the unquantised oracle
+    on 8 heads at every row."""
     w = WORKLOADS["fp8_outliers_8k"].with_(outlier_frac=0.0, outlier_mult=1.0)
     inp = make_inputs(w)
-    import torch
-    q8, k8, v8, sq, sk, sv = A.attn_fp8_prepare(*(_dev(inp[x], gpu) for x in "qkv"), _dev(inp["R"], gpu))
-    o, lse = A.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, scale=w.scale, causal=False)
-    torch.cuda.synchronize()
-    o = o.float().cpu().numpy()
-    heads = _sample_heads(w, 4, 1)
-    rows = np.unique(np.concatenate([[0, w.N - 1], np.random.default_rng(2).integers(0, w.N, 48)]))
-    err = 0.0
-    for b, h in heads:
-        oa, _ = oracle.attention_rows(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.scale, False, rows)
-        err = max(err, float(np.abs(o[b, h][rows] - oa).max()))
-    print("fp8 without outliers vs unquantised oracle: max-abs", err)
-    assert err <= TOL8
+    o, _ = _full_pipeline(inp, gpu)
+    heads = _sample_heads(w, 8, 1)
+    oa, _ = oracle_heads(inp, heads)
+    err = np.abs(np.stack([o[b, h] for b, h in heads]) - oa)
+    record_parity("fp8_no_outliers_vs_unquantised (G1)", {"max_abs": float(err.max()),
+                  "mean_abs": float(err.mean())}, gate_max_abs=TOL8, heads=len(heads), rows=w.N)
+    assert err.max() <= TOL8
+
+
+_C5 = {}
+
+
+def _literal_fp8(gpu):
+    """The literal fp8 workload (x40 outlier channels in Q, K and V), once per
+    session: the full GPU pipeline on every head; the kernel on oracle-made
+    codes of 8 heads at the full sequence length (heads are independent, so a
+    slice of heads is the same work per head); oracle B (float64 attention on
+    exactly those dequantised codes) and oracle A (the unquantised inputs) on
+    those 8 heads at every row."""
+    if not _C5:
+        w = WORKLOADS["fp8_outliers_8k"]
+        inp = make_inputs(w)
+        heads = _sample_heads(w, 8, 3)
+        o_full, _ = _full_pipeline(inp, gpu)
+        sl = {x: np.ascontiguousarray(np.stack([inp[x][b, h] for b, h in heads])[None]) for x in "qkv"}
+        cs = oracle.fp8_prepare(sl["q"], sl["k"], sl["v"], inp["R"])
+        o_codes, l_codes = _fwd_on_codes(cs, gpu, w.scale, False)
+        (q8, sq), (k8, sk), (v8, sv) = cs
+        deq = {"q": oracle.fp8_dequantize(q8, sq), "k": oracle.fp8_dequantize(k8, sk),
+               "v": oracle.fp8_dequantize(v8, sv)}
+        sl_heads = [(0, i) for i in range(len(heads))]
+        ob, lb = oracle_heads(inp, sl_heads, q=deq["q"], k=deq["k"], v=deq["v"])
+        oa, la = oracle_heads(inp, sl_heads, q=sl["q"], k=sl["k"], v=sl["v"])
+        o_full_h = np.stack([o_full[b, h] for b, h in heads])
+        _C5.update(dict(o_codes=o_codes[0], l_codes=l_codes[0], ob=ob, lb=lb, oa=oa, la=la,
+                        o_full=o_full_h, heads=heads, N=w.N))
+    return _C5
 
 
 def test_fp8_workload_literal(gpu):
-    """Gate G2 on the literal fp8 workload (outliers x40 in Q, K and V).
-
-    The kernel runs on oracle-made codes of sampled heads at the full sequence
-    length (heads are independent, so a slice of heads is the same work per
-    head) and is compared with the dequantised-input oracle.  The full
-    GPU pipeline (prepare + forward, all heads) is then compared with the
-    unquantised oracle and printed beside the input-quantisation floor; with
-    x40 outliers a softmax this peaked can also pick a different key where
-    a rotated value sits on a rounding midpoint, so that comparison is
-    reported, not gated."""
-    w = WORKLOADS["fp8_outliers_8k"]
-    inp = make_inputs(w)
-    heads = _sample_heads(w, 3, 3)
-    rows = np.unique(np.concatenate([[0, w.N - 1], np.random.default_rng(4).integers(0, w.N, 64)]))
-    sl = {x: np.ascontiguousarray(np.stack([inp[x][b, h] for b, h in heads])[None]) for x in "qkv"}
-    cs = oracle.fp8_prepare(sl["q"], sl["k"], sl["v"], inp["R"])
-    o, _ = _fwd_on_codes(cs, gpu, w.scale, False)
-    ob, _ = _oracle_b(cs, [(0, i) for i in range(len(heads))], rows, w.scale, False)
-    od = o[0][:, rows]
-    rel = np.abs(od - ob) / np.maximum(1.0, np.abs(ob))
-    print(f"fp8 literal, kernel on oracle codes vs dequantised oracle: max rel {rel.max():.4f}, "
-          f"max-abs {np.abs(od - ob).max():.4f}")
+    """Gate G2 on the literal fp8 workload: the kernel on oracle-made codes
+    against oracle B, |O - O_B| <= 6e-2 * max(1, |O_B|) at every element of 8
+    heads (every row)."""
+    c = _literal_fp8(gpu)
+    rel = np.abs(c["o_codes"] - c["ob"]) / np.maximum(1.0, np.abs(c["ob"]))
+    record_parity("fp8_outliers_8k kernel vs dequantised-input oracle (G2)",
+                  {"max_rel": float(rel.max()), "max_abs": float(np.abs(c["o_codes"] - c["ob"]).max()),
+                   "mean_abs": float(np.abs(c["o_codes"] - c["ob"]).mean()),
+                   "lse_max_abs": float(np.abs(c["l_codes"] - c["lb"]).max())},
+                  gate_max_rel=TOL8, heads=len(c["heads"]), rows=c["N"])
+    assert np.isfinite(c["o_codes"]).all()
     assert rel.max() <= TOL8
 
+
+@pytest.mark.xfail(strict=True, reason="literal fp8 gate (max-abs <= 6e-2 against the unquantised "
+                   "float64 oracle) fails: quantising the x40 outlier channels to e4m3 alone moves O "
+                   "by tens (the input-quantisation floor |O_B - O_A| is recorded beside it)")
+def test_fp8_workload_literal_vs_unquantised(gpu):
+    c = _literal_fp8(gpu)
+    err = np.abs(c["o_full"] - c["oa"])
+    floor = np.abs(c["ob"] - c["oa"])
+    record_parity("fp8_outliers_8k full pipeline vs unquantised oracle (literal)",
+                  {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                   "floor_input_quant_max": float(floor.max()),
+                   "floor_input_quant_mean": float(floor.mean())},
+                  gate_max_abs=TOL8, heads=len(c["heads"]), rows=c["N"])
+    assert err.max() <= TOL8
+
+
+def test_fwd_fp8_deterministic_and_guard_bands(gpu):
+    """Two launches give identical bits, and nothing outside O and LSE is written."""
     import torch
-    q8, k8, v8, sq, sk, sv = A.attn_fp8_prepare(*(_dev(inp[x], gpu) for x in "qkv"), _dev(inp["R"], gpu))
-    of, _ = A.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, scale=w.scale, causal=False)
+    B, H, N, d = 2, 3, 777, 128
+    inp = random_inputs(B, H, N, d, "f32", True, seed=77)
+    R = haar_orthogonal(np.random.default_rng(9).standard_normal((d, d))).astype(np.float32)
+    cs = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], R)
+    (q8, sq), (k8, sk), (v8, sv) = cs
+    args = [_dev(x, gpu) for x in (q8, k8, v8, sq, sk, sv)]
+    G, n, m = 4096, B * H * N * d, B * H * N
+    big = torch.full((n + 2 * G,), 7.0, dtype=torch.bfloat16, device=gpu)
+    lbig = torch.full((m + 2 * G,), 7.0, dtype=torch.float32, device=gpu)
+    o = big[G:G + n].view(B, H, N, d)
+    lse = lbig[G:G + m].view(B, H, N)
+    A.attn_fwd_fp8(*args, o=o, lse=lse, scale=inp["scale"], causal=True)
+    o2, l2 = A.attn_fwd_fp8(*args, scale=inp["scale"], causal=True)
     torch.cuda.synchronize()
-    of = of.float().cpu().numpy()
-    worst_a, floor_a = 0.0, 0.0
-    for i, (b, h) in enumerate(heads):
-        oa, _ = oracle.attention_rows(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], w.scale, False, rows)
-        worst_a = max(worst_a, float(np.abs(of[b, h][rows] - oa).max()))
-        floor_a = max(floor_a, float(np.abs(ob[i] - oa).max()))
-    print(f"fp8 literal, full GPU pipeline vs unquantised oracle: max-abs {worst_a:.3f} "
-          f"(input-quantisation floor {floor_a:.3f})")
+    assert (big[:G] == 7).all() and (big[G + n:] == 7).all()
+    assert (lbig[:G] == 7).all() and (lbig[G + m:] == 7).all()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+# B*H = 128 causal with fp8 K/V bytes above 1 MiB per head: each XCD walks
+# its 16 heads in two chunks of 8; every row of every head is compared
+def test_fwd_fp8_two_head_chunks_per_xcd(gpu):
+    B, H, N, d = 16, 8, 4160, 128
+    inp = random_inputs(B, H, N, d, "f32", True, seed=4300)
+    R = haar_orthogonal(np.random.default_rng(78).standard_normal((d, d))).astype(np.float32)
+    cs = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], R)
+    o, lse = _fwd_on_codes(cs, gpu, inp["scale"], True)
+    (q8, sq), (k8, sk), (v8, sv) = cs
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    ob, lb = oracle_heads(inp, heads, q=oracle.fp8_dequantize(q8, sq), k=oracle.fp8_dequantize(k8, sk),
+                          v=oracle.fp8_dequantize(v8, sv))
+    od = o.reshape(ob.shape)
+    ld = lse.reshape(lb.shape)
+    assert np.all(np.abs(od - ob) <= TOL8 * np.maximum(1.0, np.abs(ob)))
+    assert np.abs(od - ob).mean() < 5e-3
+    assert np.max(np.abs(ld - lb)) < 2e-2
 
 
 @pytest.mark.parametrize("rise", [3.0, 20.0, 100.0])
