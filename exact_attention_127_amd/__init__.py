@@ -24,7 +24,8 @@ import os
 import torch  # loads the HIP runtime that the library then shares
 
 __all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
-           "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "MX_BLOCK",
+           "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "attn_bwd_static", "MX_BLOCK",
+           "STATIC_SCRATCH_FLOATS",
            "attn_strerror", "AttnError", "AttnLibraryMissing", "lib", "LIB_PATH",
            "EXPORTED_SYMBOLS", "ATTN_F32", "ATTN_BF16", "FP8_TILE", "w4a16_gemm",
            "w4a16_dequantize", "W4A16_GROUP"]
@@ -32,14 +33,15 @@ __all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn127.so")
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
-                    "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "w4a16_gemm",
-                    "w4a16_dequantize", "attn_strerror")
+                    "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "attn_bwd_static",
+                    "w4a16_gemm", "w4a16_dequantize", "attn_strerror")
 ATTN_F32, ATTN_BF16 = 0, 1
 FP8_TILE = 128
 MX_BLOCK = 32
 W4A16_GROUP = 128
 _STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
-           -3: "ATTN_ERR_HIP"}
+           -3: "ATTN_ERR_HIP", -4: "ATTN_ERR_TOO_LARGE"}
+STATIC_SCRATCH_FLOATS = 4194304
 
 
 class AttnLibraryMissing(RuntimeError):
@@ -81,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_mxfp8.restype = _I
         L.attn_bwd.argtypes = [_P] * 10 + [_I, _I, _I, _I, _F, _I, _I, _P]
         L.attn_bwd.restype = _I
+        L.attn_bwd_static.argtypes = [_P] * 9 + [_I, _I, _I, _I, _F, _I, _I, _P]
+        L.attn_bwd_static.restype = _I
         L.w4a16_gemm.argtypes = [_P] * 5 + [_I, _I, _I, _I, _P]
         L.w4a16_gemm.restype = _I
         L.w4a16_dequantize.argtypes = [_P] * 4 + [_I, _I, _I, _P]
@@ -255,6 +259,34 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, scale
                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale_arg(scale),
                         int(bool(causal)), ATTN_BF16, _stream(stream))
     _check(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_static(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, scale=None, causal=False,
+                    stream=None):
+    """attn_bwd without the caller's scratch: the row statistic D lives in the
+    library's fixed per-GPU array (B*H*N <= STATIC_SCRATCH_FLOATS).  The C
+    call allocates nothing; pass dq, dk, dv to keep this wrapper from
+    allocating them."""
+    if q.dim() != 4:
+        raise ValueError("q, k, v, o, dout must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if q.dtype != torch.bfloat16:
+        raise ValueError("attn_bwd_static takes bfloat16 tensors")
+    for nm, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _want(t, nm, q.shape, torch.bfloat16)
+    _want(lse, "lse", (B, H, N), torch.float32)
+    for nm, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _want(t, nm, q.shape, torch.bfloat16)
+    _same_gpu(q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    st = lib().attn_bwd_static(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale_arg(scale),
+                               int(bool(causal)), ATTN_BF16, _stream(stream))
+    _check(st, "attn_bwd_static")
     return dq, dk, dv
 
 

@@ -1,11 +1,21 @@
 // C ABI of the attention library: argument checks and kernel dispatch.
 // Every check runs on the host before any HIP call, so a rejected call has
-// no device side effect; the library holds no state and allocates nothing.
+// no device side effect.  The library allocates nothing; its only state is
+// the fixed scratch array of attn_bwd_static (below) and the per-device
+// addresses of that array.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "launch.h"
+
+// Scratch memory of attn_bwd_static: the backward pass's row statistic
+// D_i = sum_c dO_ic O_ic, B*H*N floats, which attn_bwd takes from the caller.
+// Each GPU the library runs on holds its own copy for the life of the
+// process.  Host code never uses this name as an address: it looks up the
+// device address once per device (hipGetSymbolAddress) and passes that.
+static __device__ __align__(256) float scratch[ATTN_STATIC_SCRATCH_FLOATS];
 
 namespace {
 
@@ -46,6 +56,43 @@ int check_ptrs(const void* q, const void* k, const void* v, const void* o, const
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// Device address of the current device's `scratch`, looked up on the first
+// call on that device (with it current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+int scratch_address(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return ATTN_OK;
+}
+
+// Checks shared by attn_bwd and attn_bwd_static (all but the scratch
+// pointer); returns ATTN_OK, an error, or 1 for "nothing to do".
+int bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+              float* scale, int dtype) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (resolve_scale(*scale, d, scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  const void* ps[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_INVALID_ARG;
+  return st;
+}
 
 int fwd_common(bool simple, const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
@@ -163,18 +210,27 @@ int attn_fwd_mxfp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, cons
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int N,
              int d, float scale, int causal, int dtype, void* stream) {
-  int st = check_shape(B, H, N, d);
+  const int st = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, &scale, dtype);
   if (st < 0) return st;
-  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-  if (dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
-  if (resolve_scale(scale, d, &scale) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
-  const void* ps[] = {q, k, v, o, dout, dq, dk, dv};
-  for (const void* p : ps)
-    if (!p || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
-  if (!lse || !delta) return ATTN_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
-    return ATTN_ERR_INVALID_ARG;
+  if (!delta || (reinterpret_cast<uintptr_t>(delta) & 3u)) return ATTN_ERR_INVALID_ARG;
   if (st == 1) return ATTN_OK;
+  attn127::BwdArgs a{q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale,
+                     causal ? 1 : 0, stream};
+  return status_of(attn127::launch_bwd(a));
+}
+
+int attn_bwd_static(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                    float scale, int causal, int dtype, void* stream) {
+  const int st = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, &scale, dtype);
+  if (st < 0) return st;
+  if (static_cast<int64_t>(B) * H * N > ATTN_STATIC_SCRATCH_FLOATS) return ATTN_ERR_TOO_LARGE;
+  if (st == 1) return ATTN_OK;
+  float* delta = nullptr;
+  const int sa = scratch_address(&delta);
+  if (sa != ATTN_OK) return sa;
+  // D is written in full by the first of the three launches before the
+  // other two read it, so nothing left by an earlier call needs clearing
   attn127::BwdArgs a{q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale,
                      causal ? 1 : 0, stream};
   return status_of(attn127::launch_bwd(a));
@@ -202,6 +258,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size, dtype or scale)";
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    case ATTN_ERR_TOO_LARGE: return "request exceeds the library's fixed scratch buffer (attn_bwd_static: B*H*N > ATTN_STATIC_SCRATCH_FLOATS)";
     default: return "unknown status";
   }
 }

@@ -57,7 +57,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1,  /* null / misaligned pointer, bad size or scale */
   ATTN_ERR_UNSUPPORTED = -2,  /* valid request this build has no kernel for  */
-  ATTN_ERR_HIP = -3           /* the HIP runtime rejected a launch            */
+  ATTN_ERR_HIP = -3,          /* the HIP runtime rejected a launch            */
+  ATTN_ERR_TOO_LARGE = -4     /* request exceeds a fixed buffer of the library */
 } attn_status;
 
 /*
@@ -193,6 +194,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const void* dout, const float* lse, float* delta, void* dq,
              void* dk, void* dv, int B, int H, int N, int d, float scale,
              int causal, int dtype, void* stream);
+
+/* Floats of device scratch attn_bwd_static holds per GPU (16 MiB). */
+#define ATTN_STATIC_SCRATCH_FLOATS 4194304
+
+/*
+ * attn_bwd_static -- attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, kernels and results, without the delta
+ * scratch argument.  D lives instead in a fixed array of
+ * ATTN_STATIC_SCRATCH_FLOATS floats that the library holds on every GPU it
+ * runs on until the process ends; the first call on a device looks up that
+ * device's copy (the current device at the call).  The call allocates
+ * nothing.  B*H*N above ATTN_STATIC_SCRATCH_FLOATS returns ATTN_ERR_TOO_LARGE
+ * before any HIP call.  Every call on one GPU uses that GPU's single array:
+ * calls that overlap on one GPU (different streams, or host threads without
+ * ordering) race and must not be issued; calls in order on one stream are
+ * safe.  Other arguments, conventions and errors as attn_bwd.
+ */
+int attn_bwd_static(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk,
+                    void* dv, int B, int H, int N, int d, float scale,
+                    int causal, int dtype, void* stream);
 
 /* Weights per scale group of the W4A16 product. */
 #define W4A16_GROUP 128

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror():
     assert A.attn_strerror(0) == "ok"
-    for s in (-1, -2, -3):
+    for s in (-1, -2, -3, -4):
         assert len(A.attn_strerror(s)) > 5
     assert A.attn_strerror(12345) == "unknown status"
 
@@ -228,3 +228,17 @@ def test_binding_rejects_mismatched_scratch_and_gradients():
         A.w4a16_gemm(x, qw, sc, z, y=_t(1, 32, dtype=torch.float16))
     with pytest.raises(ValueError, match="scales"):
         A.w4a16_gemm(x, qw, _t(32, 3, dtype=torch.float16), z)
+
+
+def test_bwd_static_validates_on_the_host():
+    L = A.lib()
+    f = [FAKE] * 9
+    call = lambda ptrs=f, B=1, H=1, N=8, d=128, scale=0.125, dtype=1: \
+        L.attn_bwd_static(*ptrs, B, H, N, d, scale, 0, dtype, None)
+    assert call(N=A.STATIC_SCRATCH_FLOATS + 1) == -4          # beyond the fixed scratch array
+    assert call(B=2, H=4, N=A.STATIC_SCRATCH_FLOATS // 8 + 1) == -4
+    assert call(ptrs=[None] + f[1:]) == -1 and call(ptrs=f[:5] + [None] + f[6:]) == -1
+    assert call(ptrs=f[:6] + [FAKE + 8] + f[7:]) == -1         # dq misaligned
+    assert call(d=96) == -1 and call(scale=-1.0) == -1 and call(dtype=0) == -2
+    assert call(B=0) == 0 and call(N=0) == 0
+    assert "scratch" in A.attn_strerror(-4)
