@@ -25,10 +25,13 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-PEAK = {"bf16": 2500.0, "fp8": 5000.0}          # published MI355X dense TFLOP/s
+PEAK = {"bf16": 2500.0, "fp8": 5000.0,          # published MI355X dense matrix-core TFLOP/s
+        "f32": 157.3}                            # published MI355X float32 vector TFLOP/s
 HBM_PEAK_GBS = 8000.0                            # published MI355X HBM3E bandwidth
 INPUT_SET_BYTES = 512 * 10 ** 6                  # > 2x the 256 MB last-level cache
 KERNEL_SOURCES = {
+    "f32": ["exact_attention_127_amd/csrc/attn_simple.hip",
+            "exact_attention_127_amd/csrc/common.h"],
     "bf16": ["exact_attention_127_amd/csrc/attn_mfma_bf16.hip",
              "exact_attention_127_amd/csrc/device_util.h",
              "exact_attention_127_amd/csrc/common.h"],
@@ -156,6 +159,8 @@ def algorithmic_bytes(w, kind: str) -> int:
     read once, dQ, dK, dV written once, the row statistic D written and read."""
     if kind == "bwd":
         return w.B * w.H * w.N * (5 * 2 * w.d + 4 + 3 * 2 * w.d + 8)
+    if kind == "f32":
+        return w.B * w.H * w.N * (4 * 4 * w.d + 4)
     in_bytes = 2 if kind == "bf16" else 1
     scale_bytes = 3 * (w.d // 32) if kind == "mxfp8" else 0
     return w.B * w.H * w.N * (3 * in_bytes * w.d + scale_bytes + 2 * w.d + 4)
@@ -168,14 +173,16 @@ def algorithmic_flops(w, kind: str) -> float:
 def roofline(w, kind: str, kernel_ms: float, peak_tflops: float):
     """The bound that applies to one launch of workload ``w``: HBM when moving
     its algorithmic bytes at peak bandwidth takes longer than its FLOPs at
-    peak matrix-core rate, else the matrix cores."""
+    peak compute rate, else the compute units (matrix cores; the float32
+    vector ALUs for the float32 path)."""
     alg_bytes = algorithmic_bytes(w, kind)
     flops = algorithmic_flops(w, kind)
     if alg_bytes / (HBM_PEAK_GBS * 1e9) > flops / (peak_tflops * 1e12):
         roof = {"bound": "hbm", "achieved": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": round(flops / (kernel_ms * 1e-3) / 1e12, 2),
+        roof = {"bound": "alu" if kind == "f32" else "mfma",
+                "achieved": round(flops / (kernel_ms * 1e-3) / 1e12, 2),
                 "peak": round(peak_tflops, 1), "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     return roof, alg_bytes
@@ -208,10 +215,11 @@ def run_workload(name, args, fp8_scales="tile"):
             A.attn_bwd(q, k, v, o, dout, lse, dq=dq, dk=dk, dv=dv, delta=delta, scale=w.scale,
                        causal=w.causal, stream=stream)
         peak = PEAK["bf16"]
-    elif w.dtype == "bf16":
-        kind = "bf16"
-        peak = PEAK["bf16"]
-        q, k, v = (torch.from_numpy(inp[x]).to(dev).to(torch.bfloat16).contiguous() for x in "qkv")
+    elif w.dtype in ("bf16", "f32"):
+        kind = w.dtype
+        peak = PEAK[kind]
+        tdt = torch.bfloat16 if kind == "bf16" else torch.float32
+        q, k, v = (torch.from_numpy(inp[x]).to(dev).to(tdt).contiguous() for x in "qkv")
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         # an HBM-bound launch cycles through copies of its buffers, more than
@@ -245,8 +253,11 @@ def run_workload(name, args, fp8_scales="tile"):
         def step():
             forward(q8, k8, v8, sq, sk, sv, o=o, lse=lse, scale=w.scale, causal=w.causal,
                     stream=stream)
-        # scores on fp8, P V on bf16: time-weighted peak of the two halves
-        peak = 1.0 / (0.5 / PEAK["fp8"] + 0.5 / PEAK["bf16"])
+        # the dense fp8 peak; P V runs on fp16 (per-tile scales) or bf16
+        # (MXFP8) matrix cores, so a time-weighted peak of the two halves
+        # is reported beside it
+        peak = PEAK["fp8"]
+        extra_cfg["blended_peak_tflops"] = round(1.0 / (0.5 / PEAK["fp8"] + 0.5 / PEAK["bf16"]), 1)
     else:
         raise SystemExit(f"bench.py times the bf16 and fp8 workloads, not {name}")
 
@@ -254,6 +265,10 @@ def run_workload(name, args, fp8_scales="tile"):
     flops = algorithmic_flops(w, kind)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     roof, alg_bytes = roofline(w, kind, kernel_ms, peak)
+    if "blended_peak_tflops" in extra_cfg and roof["bound"] == "mfma":
+        roof["frac_of_blended_peak"] = round(roof["achieved"] / extra_cfg["blended_peak_tflops"], 4)
+    if kind == "f32":
+        extra_cfg["latency_us"] = round(kernel_ms * 1e3, 2)
     line = {
         "metric": ("attn fwd TFLOP/s + % of bf16 MFMA peak, B=1 H=16 N=16384 d=128 causal"
                    if name == "long_causal_16k" and kind != "bwd" else
@@ -386,6 +401,8 @@ def main() -> int:
         runs = [(args.workload, args.fp8_scales)]
     else:
         runs = [(n, "tile") for n in ("long_causal_16k", "vit_b16_batch64", "llm_layer_4k")]
+        if args.pass_ == "fwd":
+            runs.insert(1, ("vit_b16_single", "tile"))
         if args.pass_ == "fwd":
             runs += [("fp8_outliers_8k", "tile"), ("fp8_outliers_8k", "mx"),
                      ("w4a16_decode_70b", None), ("w4a16_batch16_70b", None)]
