@@ -14,7 +14,14 @@ The functions keep the C names:
     attn_mxfp8_prepare(q, k, v, R)             -> (q8, k8, v8, sq, sk, sv)  E8M0 per 32 channels
     attn_fwd_mxfp8(q8, k8, v8, sq, sk, sv, ...) -> (o, lse)
     attn_bwd(q, k, v, o, dout, lse, ...)       -> (dq, dk, dv)
+    attn_bwd_static(q, k, v, o, dout, lse, ...) -> (dq, dk, dv)  no scratch argument
+    w4a16_gemm(x, qweight, scales, zeros)      -> y
+    w4a16_dequantize(qweight, scales, zeros)   -> w
     attn_strerror(status)
+
+Every wrapper checks the shape, dtype, contiguity and device of each tensor it
+is given (outputs and scratch buffers included) and raises ValueError before
+anything reaches the library.
 """
 from __future__ import annotations
 

@@ -17,8 +17,8 @@
 // relative to the largest V tile scale of the head, rides on P:
 // p * s_v / s_vmax is rounded to fp16 (2^-11 of each weight; it stays below
 // 2^8, far inside fp16's range).  Rounding P to e4m3 instead would cost up
-// to 2^-4 of every weight and bf16 2^-9; where the x40 outlier channels of V
-// cancel in O, a 2^-9 weight error reaches 9% of |O| (measured on the fp8
+// to 2^-4 of every weight and bf16 2^-8; where the x40 outlier channels of V
+// cancel in O, a 2^-8 weight error reaches 9% of |O| (measured on the fp8
 // workload against float64 attention on the dequantised codes), 2^-11 about
 // 1%.
 #include <math.h>

@@ -6,7 +6,7 @@ Errors are measured relative to the size of each gradient tensor:
     rel_max  = max |G - R| / max |R|,     rel_mean = mean |G - R| / mean |R|.
 Where the tolerances come from:
   * P and dS enter the products rounded to bf16 and the outputs are rounded
-    to bf16 (2^-9 relative each): about 2.3e-3 mean on short rows, as
+    to bf16 (unit roundoff 2^-8 each): about 2.3e-3 mean on short rows, as
     measured, and up to ~4e-3 where dQ is mostly cancellation (N = 2).
   * D = rowsum(dO * O) is formed from the stored bf16 O, as the method keeps
     O and the row statistic rather than S.  Its error does not average out

@@ -9,8 +9,8 @@ the float64 oracle.
   rounding midpoint.
 * attn_fwd_mxfp8 on oracle-made codes against float64 attention on exactly
   the dequantised inputs ("oracle B").  Widening V to bf16 is exact, so the
-  remaining error is the bf16 rounding of P (<= 2^-9 of each weight, i.e.
-  <= 2^-9 * (P|V|) per output) and of O (<= 2^-9 |O|), allowed twice over,
+  remaining error is the bf16 rounding of P (at most u = 2^-8, bf16's unit
+  roundoff, of each weight, i.e. <= u (P|V|) per output) and of O (<= u |O|),
   plus the float32 sums inside the score instruction: a sum of d exact
   products rounded faithfully at every step (any rounding mode) errs by at
   most d 2^-23 sum|q_c k_c| <= d 2^-23 |q| |k|, which moves each weight p by
@@ -117,8 +117,8 @@ def _acc_delta(qd, kd, scale):
 
 
 def _bound(cs, heads, rows, scale, causal):
-    """2^-8 (P|V|) + 2^-8 |O_B| + 2 (e^delta - 1) (P|V|): twice the bf16
-    rounding of P and of O, and the float32 sums of the scores."""
+    """2^-8 (P|V|) + 2^-8 |O_B| + 2 (e^delta - 1) (P|V|): the bf16 rounding
+    (unit roundoff 2^-8) of P and of O, and the float32 sums of the scores."""
     (q8, sq), (k8, sk), (v8, sv) = cs
     qd, kd, vd = (oracle.dequantize_mx(c, s) for c, s in ((q8, sq), (k8, sk), (v8, sv)))
     bs = []
