@@ -229,12 +229,15 @@ def run_workload(name, args, fp8_scales="tile"):
             n_sets = -(-INPUT_SET_BYTES // algorithmic_bytes(w, kind))
             bufs += [tuple(t.clone() for t in bufs[0]) for _ in range(n_sets - 1)]
         extra_cfg["input_sets"] = len(bufs)
+        # arguments checked once per buffer set: a launch is then one C call,
+        # so the host keeps up with the 20-30 us kernels of short sequences
+        launchers = [A.attn_fwd_launcher(qi, ki, vi, oi, li, scale=w.scale, causal=w.causal,
+                                         stream=stream) for (qi, ki, vi, oi, li) in bufs]
         turn = [0]
 
         def step():
-            qi, ki, vi, oi, li = bufs[turn[0] % len(bufs)]
+            launchers[turn[0] % len(launchers)]()
             turn[0] += 1
-            A.attn_fwd(qi, ki, vi, o=oi, lse=li, scale=w.scale, causal=w.causal, stream=stream)
     elif w.dtype == "fp8":
         mx = fp8_scales == "mx"
         kind = "mxfp8" if mx else "fp8"

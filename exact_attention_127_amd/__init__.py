@@ -8,6 +8,7 @@ and a missing library raises ``AttnLibraryMissing``.
 The functions keep the C names:
 
     attn_fwd(q, k, v, o=None, lse=None, scale=None, causal=False)
+    attn_fwd_launcher(q, k, v, o, lse, ...)    -> launch(): attn_fwd again, no checks
     attn_fwd_simple(...)                       same contract, plain kernel
     attn_fp8_prepare(q, k, v, R)               -> (q8, k8, v8, sq, sk, sv)
     attn_fwd_fp8(q8, k8, v8, sq, sk, sv, ...)  -> (o, lse)
@@ -30,7 +31,7 @@ import os
 
 import torch  # loads the HIP runtime that the library then shares
 
-__all__ = ["attn_fwd", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
+__all__ = ["attn_fwd", "attn_fwd_launcher", "attn_fwd_simple", "attn_fp8_prepare", "attn_fwd_fp8",
            "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "attn_bwd_static", "MX_BLOCK",
            "STATIC_SCRATCH_FLOATS",
            "attn_strerror", "AttnError", "AttnLibraryMissing", "lib", "LIB_PATH",
@@ -185,6 +186,25 @@ def _fwd(name, q, k, v, o, lse, scale, causal, stream, with_lse):
 def attn_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None, with_lse=True):
     """O (and LSE) of softmax(Q K^T * scale) V on matrix cores (bf16) or in float32."""
     return _fwd("attn_fwd", q, k, v, o, lse, scale, causal, stream, with_lse)
+
+
+def attn_fwd_launcher(q, k, v, o, lse=None, scale=None, causal=False, stream=None):
+    """Checks the arguments of attn_fwd once and returns a callable that
+    launches it again on the same buffers and stream.  Each launch then costs
+    one C call on the host, for loops whose kernels take less time than the
+    per-call checks (short sequences); the buffers must stay alive."""
+    _fwd("attn_fwd", q, k, v, o, lse, scale, causal, stream, lse is not None)
+    B, H, N, d = q.shape
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F32
+    fn = lib().attn_fwd
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale_arg(scale),
+            int(bool(causal)), dtype, _stream(stream))
+
+    def launch():
+        st = fn(*args)
+        if st != 0:
+            raise AttnError(st, "attn_fwd")
+    return launch
 
 
 def attn_fwd_simple(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None,

@@ -473,6 +473,66 @@ __device__ __forceinline__ void phase_b(WaveState<D>& w, f32x16 (&snext)[BC / 32
   }
   lenext = l0 + l1;
 }
+
+// Work item of workgroup `id`: XCD-grouped heads, heaviest causal blocks
+// first.  When B*H is a multiple of 8, XCD x takes heads x, x+8, ...;
+// causal launches walk them in chunks of hc heads, each chunk's query blocks
+// heaviest first and interleaved across its heads.
+__device__ __forceinline__ void work_item(int id, int BH, int nqb, bool causal, int hc, int& bh, int& qb) {
+  if (BH % kXcds == 0) {
+    const int x = id % kXcds, s = id / kXcds;
+    if (causal) {
+      const int per = hc * nqb, ch = s / per, r = s - ch * per;
+      qb = nqb - 1 - r / hc;
+      bh = x + kXcds * (ch * hc + r % hc);
+    } else {
+      bh = x + kXcds * (s / nqb); qb = s % nqb;
+    }
+  } else if (causal) {
+    qb = nqb - 1 - id / BH; bh = id % BH;
+  } else {
+    bh = id / nqb; qb = id % nqb;
+  }
+}
+
+// The wave's 32 query rows as the B operand of the score products (rows
+// past N read as zero through the buffer bounds).
+template <int D>
+__device__ __forceinline__ void load_q(WaveState<D>& w, const uint16_t* q, int64_t base, int q0w, int N,
+                                       int j, int h) {
+  const int rows = max(0, min(BRW, N - q0w));
+  const auto rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(q + base + static_cast<int64_t>(min(q0w, N)) * D), 0,
+      static_cast<int>(rows * 2 * D), 0x00020000);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, j * 2 * D + (ks * 16 + 8 * h) * 2, 0, 0);
+    w.qr[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+// Epilogue: the deferred division by the normaliser, bf16 O, natural-log LSE.
+template <int D>
+__device__ __forceinline__ void store_rows(const WaveState<D>& w, uint16_t* o, float* lse, int64_t base,
+                                           int bh, int N, int qrow, int h) {
+  const float ltot = halves_sum(w.lsum);
+  if (qrow < N) {
+    const float inv = 1.f / ltot;
+    uint16_t* orow = o + base + static_cast<int64_t>(qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = db * 32 + 8 * g + 4 * h;
+        u32x2 wv;
+        wv[0] = pack_bf16x2(w.oacc[db][4 * g + 0] * inv, w.oacc[db][4 * g + 1] * inv);
+        wv[1] = pack_bf16x2(w.oacc[db][4 * g + 2] * inv, w.oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + col) = wv;
+      }
+    if (lse != nullptr && h == 0)
+      lse[static_cast<int64_t>(bh) * N + qrow] = (w.m + __log2f(ltot)) * kLn2;
+  }
+}
 #endif  // __HIP_DEVICE_COMPILE__
 
 // The causal flag is a run-time argument: the causal and non-causal launches
@@ -498,25 +558,8 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int j = lane & 31;        // query column inside the wave's 32 rows
   const int h = lane >> 5;        // lane half
 
-  // ---- work item: XCD-grouped heads, heaviest causal blocks first ----
-  const int id = static_cast<int>(blockIdx.x);
   int bh, qb;
-  if (BH % kXcds == 0) {
-    // XCD x takes heads x, x+8, ...; causal: in chunks of hc heads, each
-    // chunk's query blocks heaviest first (interleaved across its heads)
-    const int x = id % kXcds, s = id / kXcds;
-    if (causal) {
-      const int per = hc * nqb, ch = s / per, r = s - ch * per;
-      qb = nqb - 1 - r / hc;
-      bh = x + kXcds * (ch * hc + r % hc);
-    } else {
-      bh = x + kXcds * (s / nqb); qb = s % nqb;
-    }
-  } else if (causal) {
-    qb = nqb - 1 - id / BH; bh = id % BH;
-  } else {
-    bh = id / nqb; qb = id % nqb;
-  }
+  work_item(static_cast<int>(blockIdx.x), BH, nqb, causal, hc, bh, qb);
   const int q0 = qb * BR;
   const int q0w = q0 + wave * BRW;
   const int qrow = q0w + j;
@@ -542,17 +585,7 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   issue_copy<D, NW, false>(kring_a, kbase, 0, N, wave, lane);
   issue_copy<D, NW, true>(vring_a, vbase, 0, N, wave, lane);
   if (ntiles > 1) issue_copy<D, NW, false>(kring_a + C::TILEB, kbase, BC, N, wave, lane);
-  {
-    const int rows = max(0, min(BRW, N - q0w));
-    const auto rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q + base + static_cast<int64_t>(min(q0w, N)) * D), 0,
-        static_cast<int>(rows * C::ROWB), 0x00020000);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, j * C::ROWB + (ks * 16 + 8 * h) * 2, 0, 0);
-      w.qr[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
+  load_q<D>(w, q, base, q0w, N, j, h);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -600,24 +633,7 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (t + 1 < ntiles) iteration(t + 1, sb, sa, peb, pea, leb, lea);
   }
 
-  // ---- epilogue: the deferred division, bf16 output, LSE ----
-  const float ltot = halves_sum(w.lsum);
-  if (qrow < N) {
-    const float inv = 1.f / ltot;
-    uint16_t* orow = o + base + static_cast<int64_t>(qrow) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = db * 32 + 8 * g + 4 * h;
-        u32x2 wv;
-        wv[0] = pack_bf16x2(w.oacc[db][4 * g + 0] * inv, w.oacc[db][4 * g + 1] * inv);
-        wv[1] = pack_bf16x2(w.oacc[db][4 * g + 2] * inv, w.oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + col) = wv;
-      }
-    if (lse != nullptr && h == 0)
-      lse[static_cast<int64_t>(bh) * N + qrow] = (w.m + __log2f(ltot)) * kLn2;
-  }
+  store_rows<D>(w, o, lse, base, bh, N, qrow, h);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -636,13 +652,235 @@ hipError_t launch_one(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
+
+// ---- d = 64: one tile at a time, three workgroups per CU ----
+//
+// At d=64 a 32x32x16 product covers half as many channels, so each score
+// costs half the matrix work but the same vector work (scaling, exp2,
+// normaliser, bf16 pack) as at d=128; the short rows of an image model add a
+// prologue and a masked last tile per handful of tiles.  Software pipelining
+// inside a wave needs two score buffers (182 VGPRs, two waves per SIMD);
+// running each wave's tiles one after another needs 140, so three
+// workgroups share a CU and the SIMDs overlap one wave's matrix work with
+// another's vector work instead.  Measured side by side against the
+// pipelined kernel at d=64, identical results: B=64 H=12 N=196 0.0280 ->
+// 0.0233 ms (0.0257 -> 0.0212 causal); N=512 to 8192, causal or not, 2-7 %
+// faster.  A wave also skips the second 32-key block of a tile (its score
+// and P V products and exponentials) when every key in it is masked for all
+// its rows: the last tile of a 196-key row holds 4 keys.
+#if defined(__HIP_DEVICE_COMPILE__)
+constexpr int kSeqReadAhead = 3;   // LDS operands in flight
+
+// S^T for the first NKB 32-key blocks of a tile, operand reads 3 MFMAs ahead.
+template <int D, int NKB>
+__device__ __forceinline__ void scores_seq(f32x16 (&sacc)[BC / 32], const WaveState<D>& w,
+                                           const LaneAddr<D>& la, const char* kst) {
+  constexpr int NM = NKB * (D / 16), RA = kSeqReadAhead;
+  bf16x8 kop[NM];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < RA && i < NM; ++i) kop[i] = k_operand<D>(kst, la, i);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i + RA < NM) kop[i + RA] = k_operand<D>(kst, la, i + RA);
+    const int kb = i / (D / 16), ks = i % (D / 16);
+    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], w.qr[ks], ks == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// O^T += V^T P^T over the first NKB 32-key blocks (key steps c16 < 2*NKB).
+template <int D, int NKB>
+__device__ __forceinline__ void pv_seq(WaveState<D>& w, const LateWords& pl, const EarlyWords& pe,
+                                       const LaneAddr<D>& la, const char* vst) {
+  constexpr int NM = (D / 32) * 2 * NKB, RA = kSeqReadAhead;
+  // n-th product: channel block n / (2*NKB), key step n % (2*NKB)
+  auto op_index = [](int n) { return (n / (2 * NKB)) * (BC / 16) + n % (2 * NKB); };
+  bf16x8 vop[NM];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < RA && n < NM; ++n) vop[n] = v_operand<D>(vst, la, op_index(n));
+#pragma unroll
+  for (int n = 0; n < NM; ++n) {
+    if (n + RA < NM) vop[n + RA] = v_operand<D>(vst, la, op_index(n + RA));
+    const int i = op_index(n), db = i / (BC / 16), c16 = i % (BC / 16);
+    w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[n], p_operand(pl, pe, c16), w.oacc[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int NKB>
+__device__ __forceinline__ float tile_max_seq(const f32x16 (&s)[BC / 32]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  return mx;
+}
+
+// Numerators of the pairs in the first NKB key blocks, summed in the same
+// grouping as the pipelined kernel (late pairs, then early pairs): p = 0 for
+// the skipped block, so both kernels give the same bits.
+template <int NKB>
+__device__ __forceinline__ void words_seq(LateWords& pl, EarlyWords& pe, float& ll, float& le,
+                                          const f32x16 (&t)[BC / 32]) {
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kLate; ++j)
+    if (late_pair(j) / 8 < NKB) exp_pair(pl.w[late_pair(j)], ls0, ls1, t, late_pair(j));
+  ll = ls0 + ls1;
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < kEarly; ++k)
+    if (early_pair(k) / 8 < NKB) exp_pair(pe.w[k], l0, l1, t, early_pair(k));
+  le = l0 + l1;
+}
+
+// One tile: scores, mask, exponents against the reference (the first tile's
+// maximum; moved only when the numerators would pass 2^16, as in the
+// pipelined kernel), numerators, P V.
+template <int D, int NKB>
+__device__ __forceinline__ void tile_seq(WaveState<D>& w, const LaneAddr<D>& la, const char* kst,
+                                         const char* vst, int kv0, int N, int qrow, int h, bool causal,
+                                         bool need_mask, bool first, float c) {
+  f32x16 s[BC / 32];
+  scores_seq<D, NKB>(s, w, la, kst);
+  if (need_mask) {
+    const int lim = key_limit(kv0, N, qrow, h, causal);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = key_off(kb, r) > lim ? -INFINITY : s[kb][r];
+  }
+  if (first) w.m = halves_max(tile_max_seq<NKB>(s)) * c;
+  const float mref = (w.m == -INFINITY) ? 0.f : w.m;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -mref);
+  LateWords pl;
+  EarlyWords pe;
+  float ll, le;
+  words_seq<NKB>(pl, pe, ll, le, s);
+  if (tile_overflows<D>(ll + le)) {
+    const float delta = fmaxf(halves_max(tile_max_seq<NKB>(s)), 0.f);
+    const float alpha = fast_exp2(-delta);
+    w.lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) w.oacc[db] *= alpha;
+    w.m += delta;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
+    words_seq<NKB>(pl, pe, ll, le, s);
+  }
+  w.lsum += ll + le;
+  pv_seq<D, NKB>(w, pl, pe, la, vst);
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
+template <int D>
+__global__ void __launch_bounds__(256, 3)
+attn_mfma_bf16_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                          float* __restrict__ lse, int N, int BH, int nqb, float c, int causal_arg, int hc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = 4;
+  using C = Cfg<D, NW>;
+  constexpr int BR = C::BR;
+  const bool causal = causal_arg != 0;
+  // two-slot rings for K and V tiles
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILEB];
+  char* const kring = smem;
+  char* const vring = smem + 2 * C::TILEB;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+
+  int bh, qb;
+  work_item(static_cast<int>(blockIdx.x), BH, nqb, causal, hc, bh, qb);
+  const int q0 = qb * BR;
+  const int q0w = q0 + wave * BRW;
+  const int qrow = q0w + j;
+  const int64_t base = static_cast<int64_t>(bh) * N * D;
+  const uint16_t* kbase = k + base;
+  const uint16_t* vbase = v + base;
+
+  WaveState<D> w;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) w.oacc[db] = f32x16{};
+  w.m = -INFINITY;
+  w.lsum = 0.f;
+  const LaneAddr<D> la(j, h, lane);
+
+  const int kend = causal ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+  // last tile this wave needs (-1: the wave's rows are all past the end),
+  // and its last visible key
+  int last = -1;
+  if (q0w < N) last = causal ? min(ntiles - 1, (q0w + BRW - 1) / BC) : ntiles - 1;
+  const int kmax = causal ? min(N - 1, q0w + BRW - 1) : N - 1;
+
+  const uint32_t kring_a = lds_addr(kring), vring_a = lds_addr(vring);
+  issue_copy<D, NW, false>(kring_a, kbase, 0, N, wave, lane);
+  issue_copy<D, NW, true>(vring_a, vbase, 0, N, wave, lane);
+  load_q<D>(w, q, base, q0w, N, j, h);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // At the top of iteration t, K and V of tile t are in ring slot t&1; the
+  // iteration copies tile t+1 into the other slot, which every wave left at
+  // the previous barrier.
+  for (int t = 0; t < ntiles; ++t) {
+    const int kv0 = t * BC;
+    if (t + 1 < ntiles) {
+      issue_copy<D, NW, false>(kring_a + ((t + 1) & 1) * C::TILEB, kbase, kv0 + BC, N, wave, lane);
+      issue_copy<D, NW, true>(vring_a + ((t + 1) & 1) * C::TILEB, vbase, kv0 + BC, N, wave, lane);
+    }
+    if (t <= last) {
+      const char* kst = kring + (t & 1) * C::TILEB;
+      const char* vst = vring + (t & 1) * C::TILEB;
+      const bool need_mask = (causal && kv0 + BC - 1 > q0w) || (kv0 + BC > N);
+      if (kv0 + 32 > kmax)
+        tile_seq<D, 1>(w, la, kst, vst, kv0, N, qrow, h, causal, need_mask, t == 0, c);
+      else
+        tile_seq<D, 2>(w, la, kst, vst, kv0, N, qrow, h, causal, need_mask, t == 0, c);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  store_rows<D>(w, o, lse, base, bh, N, qrow, h);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int D>
+hipError_t launch_seq(const LaunchArgs& a) {
+  using C = Cfg<D, 4>;
+  const int BH = a.B * a.H;
+  const int nqb = (a.N + C::BR - 1) / C::BR;
+  const int64_t blocks = static_cast<int64_t>(nqb) * BH;
+  const int hc = causal_head_chunk(BH, 4LL * a.N * D);      // K and V bytes of a head
+  hipLaunchKernelGGL((attn_mfma_bf16_seq_kernel<D>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(C::NT), 0, static_cast<hipStream_t>(a.stream),
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                     a.N, BH, nqb, a.scale * kLog2e, a.causal, hc);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// d = 128: eight waves (two per SIMD, one K/V tile copy shared by 256 query
-// rows) measured faster than four.  d = 64 (short sequences): four waves,
-// 128 rows per workgroup and two workgroups per CU.
+// d = 128: the pipelined kernel with eight waves (two per SIMD, one K/V tile
+// copy shared by 256 query rows), measured faster than four.  d = 64: the
+// one-tile-at-a-time kernel, three four-wave workgroups per CU.
 hipError_t launch_mfma_bf16(const LaunchArgs& a) {
-  return a.d == 64 ? launch_one<64, 4>(a) : launch_one<128, 8>(a);
+  return a.d == 64 ? launch_seq<64>(a) : launch_one<128, 8>(a);
 }
 
 }  // namespace attn127

@@ -155,6 +155,8 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         A.attn_fwd_simple(q, q, q)
     with pytest.raises(ValueError, match="GPU"):
+        A.attn_fwd_launcher(q, q, q, q.clone())
+    with pytest.raises(ValueError, match="GPU"):
         A.attn_bwd(q, q, q, q, q, _t(1, 2, 8, dtype=torch.float32))
     f = _t(1, 2, 8, 64, dtype=torch.float32)
     with pytest.raises(ValueError, match="GPU"):
@@ -202,6 +204,8 @@ def test_binding_rejects_mismatched_outputs(bad):
         v = _t(1, 2, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         A.attn_fwd(q, k, v, o=o, lse=lse)
+    with pytest.raises(ValueError):
+        A.attn_fwd_launcher(q, k, v, o, lse)
 
 
 def test_binding_rejects_mismatched_scratch_and_gradients():

@@ -22,7 +22,7 @@ LLVM = "/opt/rocm/llvm/bin"
 # kernel (demangled-name fragment) -> (VGPRs, LDS bytes) as quoted in the design notes
 QUOTED = {
     "attn_mfma_bf16_kernelILi128ELi8E": (239, 65536),
-    "attn_mfma_bf16_kernelILi64ELi4E": (182, 32768),
+    "attn_mfma_bf16_seq_kernelILi64E": (146, 32768),
     "attn_fp8_kernelILi128ELi8ELb0ELb0E": (163, 57344),
     "bwd_dkdv_kernelILi128ELi8E": (246, 132096),
     "bwd_dq_kernelILi128ELi8E": (256, 98304),
@@ -71,6 +71,16 @@ def test_eight_wave_kernels_fit_two_waves_per_simd():
             total = -(-k["vgpr"] // 4) * 4 + k["agpr"]
             assert total <= 256, k
             assert k["lds"] <= 160 * 1024, k
+
+
+def test_d64_forward_fits_three_workgroups_per_cu():
+    # the one-tile-at-a-time d=64 kernel relies on three four-wave workgroups
+    # per CU: at most 168 VGPRs (8-register granule) and a third of the LDS
+    hit = [k for k in _kernels() if "attn_mfma_bf16_seq_kernel" in k["name"]]
+    assert hit
+    for k in hit:
+        assert -(-k["vgpr"] // 8) * 8 + k["agpr"] <= 168, k
+        assert 3 * k["lds"] <= 160 * 1024, k
 
 
 def test_quoted_register_and_lds_figures():

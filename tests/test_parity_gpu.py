@@ -262,6 +262,25 @@ def test_default_scale_is_inverse_sqrt_d(gpu, d):
         assert (l1 - l2).abs().max().item() <= 1e-5
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_launcher_matches_attn_fwd(gpu, dtype):
+    """attn_fwd_launcher checks once and relaunches attn_fwd on the same buffers."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    inp = random_inputs(2, 3, 196, 64, dtype, False, seed=15)
+    q, k, v = (to_device(inp[x], tdt, gpu) for x in "qkv")
+    o1, l1 = A.attn_fwd(q, k, v, scale=inp["scale"])
+    o2, l2 = torch.full_like(o1, 7), torch.full_like(l1, 7)
+    launch = A.attn_fwd_launcher(q, k, v, o2, l2, scale=inp["scale"])
+    launch()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o2.fill_(7)
+    launch()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
 def test_deterministic_and_lse_optional(gpu):
     import torch
     inp = random_inputs(1, 4, 777, 128, "bf16", True, seed=4)
