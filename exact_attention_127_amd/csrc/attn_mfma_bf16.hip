@@ -681,7 +681,13 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   int bh, qb;
   work_item(static_cast<int>(blockIdx.x), BH, nqb, causal, hc, bh, qb);
   const int q0 = qb * BR;
-  const int q0w = q0 + wave * BRW;
+  // Row block of this wave.  The waves of a workgroup are placed on the four
+  // SIMDs in turn (waves w and w+4 share one), and under the causal mask a
+  // block's lower rows need fewer tiles; pairing row blocks r and 7-r on a
+  // SIMD gives every SIMD the same number of idle wave-tiles at the diagonal
+  // (measured: 4k layer 1.0547 -> 1.0485 ms, 16k 0.9167 -> 0.9145 ms).
+  const int rgp = NW == 8 ? (wave < 4 ? wave : 11 - wave) : wave;
+  const int q0w = q0 + rgp * BRW;
   const int qrow = q0w + j;
   const int64_t base = static_cast<int64_t>(bh) * N * D;
   const uint16_t* kbase = k + base;
@@ -829,7 +835,13 @@ attn_mfma_bf16_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __rest
   int bh, qb;
   work_item(static_cast<int>(blockIdx.x), BH, nqb, causal, hc, bh, qb);
   const int q0 = qb * BR;
-  const int q0w = q0 + wave * BRW;
+  // Row block of this wave.  The waves of a workgroup are placed on the four
+  // SIMDs in turn (waves w and w+4 share one), and under the causal mask a
+  // block's lower rows need fewer tiles; pairing row blocks r and 7-r on a
+  // SIMD gives every SIMD the same number of idle wave-tiles at the diagonal
+  // (measured: 4k layer 1.0547 -> 1.0485 ms, 16k 0.9167 -> 0.9145 ms).
+  const int rgp = NW == 8 ? (wave < 4 ? wave : 11 - wave) : wave;
+  const int q0w = q0 + rgp * BRW;
   const int qrow = q0w + j;
   const int64_t base = static_cast<int64_t>(bh) * N * D;
   const uint16_t* kbase = k + base;
