@@ -232,7 +232,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   } else {
     bh = id / nqb; qb = id % nqb;
   }
-  const int q0 = qb * BR, q0w = q0 + wave * 32, qrow = q0w + j;
+  // row blocks r and 7-r share a SIMD (waves w and w+4 do), so the causal
+  // diagonal leaves every SIMD the same idle work, as in the forward kernel
+  const int rgp = NW == 8 ? (wave < 4 ? wave : 11 - wave) : wave;
+  const int q0 = qb * BR, q0w = q0 + rgp * 32, qrow = q0w + j;
   const int64_t base = static_cast<int64_t>(bh) * N * D;
   const uint16_t* kbase = k + base;
   const uint16_t* vbase = v + base;
