@@ -124,9 +124,10 @@ int attn_fp8_prepare(const float* q, const float* k, const float* v,
  * units, inputs block-quantised with one scale per tile).
  * Value of an input element = decode(code) * scale of its 128-token tile.
  * Q K^T runs on fp8 MFMA (e4m3 x e4m3, float32 accumulation) with the Q and
- * K tile scales folded into the exponent's multiplier.  P V runs on bf16
- * MFMA: each e4m3 V tile is widened to bf16 (exact) in LDS, and P, carrying
- * the V tile's scale, is rounded to bf16 (nearest-even).  o is bf16
+ * K tile scales folded into the exponent's multiplier.  P V runs on fp16
+ * MFMA: each e4m3 V operand is widened to fp16 (exact) in registers, and P,
+ * carrying the V tile's scale relative to the head's largest V tile scale,
+ * is rounded to fp16 (nearest-even).  o is bf16
  * [B][H][N][d]; lse (nullable) float32 [B][H][N].  Other conventions as
  * attn_fwd.
  */
