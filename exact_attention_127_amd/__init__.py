@@ -17,6 +17,7 @@ The functions keep the C names:
     attn_bwd(q, k, v, o, dout, lse, ...)       -> (dq, dk, dv)
     attn_bwd_static(q, k, v, o, dout, lse, ...) -> (dq, dk, dv)  no scratch argument
     w4a16_gemm(x, qweight, scales, zeros)      -> y
+    w4a16_gemm_launcher(x, qweight, scales, zeros, y) -> launch(): w4a16_gemm again, no checks
     w4a16_dequantize(qweight, scales, zeros)   -> w
     attn_strerror(status)
 
@@ -35,7 +36,7 @@ __all__ = ["attn_fwd", "attn_fwd_launcher", "attn_fwd_simple", "attn_fp8_prepare
            "attn_mxfp8_prepare", "attn_fwd_mxfp8", "attn_bwd", "attn_bwd_static", "MX_BLOCK",
            "STATIC_SCRATCH_FLOATS",
            "attn_strerror", "AttnError", "AttnLibraryMissing", "lib", "LIB_PATH",
-           "EXPORTED_SYMBOLS", "ATTN_F32", "ATTN_BF16", "FP8_TILE", "w4a16_gemm",
+           "EXPORTED_SYMBOLS", "ATTN_F32", "ATTN_BF16", "FP8_TILE", "w4a16_gemm", "w4a16_gemm_launcher",
            "w4a16_dequantize", "W4A16_GROUP"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -392,6 +393,22 @@ def w4a16_gemm(x, qweight, scales, zeros, y=None, group=W4A16_GROUP, stream=None
                           int(group), _stream(stream))
     _check(st, "w4a16_gemm")
     return y
+
+
+def w4a16_gemm_launcher(x, qweight, scales, zeros, y, group=W4A16_GROUP, stream=None):
+    """Checks the arguments of w4a16_gemm once and returns a callable that
+    launches it again on the same buffers and stream (one C call each)."""
+    w4a16_gemm(x, qweight, scales, zeros, y=y, group=group, stream=stream)
+    M, K = x.shape
+    N = qweight.shape[0]
+    fn = lib().w4a16_gemm
+    args = (_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), M, N, K, int(group), _stream(stream))
+
+    def launch():
+        st = fn(*args)
+        if st != 0:
+            raise AttnError(st, "w4a16_gemm")
+    return launch
 
 
 def w4a16_dequantize(qweight, scales, zeros, K, w=None, group=W4A16_GROUP, stream=None):

@@ -177,6 +177,8 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         A.w4a16_gemm(x, qw, sc, z)
     with pytest.raises(ValueError, match="GPU"):
+        A.w4a16_gemm_launcher(x, qw, sc, z, _t(1, 32, dtype=torch.float16))
+    with pytest.raises(ValueError, match="GPU"):
         A.w4a16_dequantize(qw, sc, z, 256)
 
 

@@ -121,6 +121,23 @@ def test_deterministic(gpu):
     assert np.array_equal(_gemm(inp, gpu), _gemm(inp, gpu))
 
 
+def test_launcher_matches_w4a16_gemm(gpu):
+    """w4a16_gemm_launcher checks once and relaunches w4a16_gemm on the same buffers."""
+    import torch
+    inp = _case(3, 96, 1024, 12)
+    args = _dev(inp, gpu)
+    y1 = A.w4a16_gemm(*args)
+    y2 = torch.full_like(y1, 7)
+    launch = A.w4a16_gemm_launcher(*args, y2)
+    launch()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    y2.fill_(7)
+    launch()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
 @pytest.mark.parametrize("name", ["w4a16_decode_70b", "w4a16_batch16_70b"])
 def test_full_size_sampled_columns(gpu, name):
     inp = make_w4a16_inputs(name)
