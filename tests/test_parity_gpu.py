@@ -61,6 +61,16 @@ def test_mfma_bf16_small(gpu, N, d, causal):
     _check_full(A.attn_fwd, inp, gpu, "bf16", small=True)
 
 
+# d=128 rows of more than 512 keys on average (non-causal N > 512, causal
+# N > 1024) take the software-pipelined kernel, shorter ones the
+# one-tile-at-a-time kernel: ragged tails and the causal diagonal of both
+@pytest.mark.parametrize("N", [513, 577, 1000, 1100])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mfma_bf16_d128_both_kernels(gpu, N, causal):
+    inp = random_inputs(2, 3, N, 128, "bf16", causal, seed=900 + N + causal)
+    _check_full(A.attn_fwd, inp, gpu, "bf16", small=True)
+
+
 # B*H a multiple of 8: the grid gives each XCD whole heads and, when causal,
 # walks chunks of heads heaviest query block first (chunks of 2 and 3 heads
 # here); every row is compared, so a work item mapped twice or never fails.
@@ -220,15 +230,15 @@ def _rising_inputs(N, d, causal, rise, seed):
 
 
 @pytest.mark.parametrize("rise", [3.0, 20.0, 100.0])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d,N", [(64, 300), (128, 300), (128, 1100)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_rising_scores_move_the_reference(gpu, rise, d, causal):
+def test_rising_scores_move_the_reference(gpu, rise, d, N, causal):
     """Each key tile's numerators outgrow the exponent reference that earlier
     tiles set: at 3 per 64 keys the reference moves every few tiles, at 20
     every tile, and at 100 (144 in base 2) the numerators against the old
     reference would not even be finite in float32.  The kernel's overflow
     path must take the tile's own maximum as the new reference each time."""
-    inp = _rising_inputs(300, d, causal, rise, seed=int(rise) * 10 + d + causal)
+    inp = _rising_inputs(N, d, causal, rise, seed=int(rise) * 10 + d + causal)
     _check_full(A.attn_fwd, inp, gpu, "bf16", small=True)
 
 
@@ -294,7 +304,7 @@ def test_deterministic_and_lse_optional(gpu):
 
 
 @pytest.mark.parametrize("fn", [A.attn_fwd, A.attn_fwd_simple])
-@pytest.mark.parametrize("N,d,causal", [(196, 64, False), (777, 128, True)])
+@pytest.mark.parametrize("N,d,causal", [(196, 64, False), (777, 128, True), (1100, 128, True)])
 def test_guard_bands_untouched(gpu, fn, N, d, causal):
     import torch
     B, H = 1, 3
