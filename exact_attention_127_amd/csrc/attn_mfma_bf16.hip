@@ -795,21 +795,22 @@ hipError_t launch_one(const LaunchArgs& a) {
 }
 
 
-// ---- d = 64: one tile at a time, three workgroups per CU ----
+// ---- one tile at a time: d = 64, and short rows at d = 128 ----
 //
 // At d=64 a 32x32x16 product covers half as many channels, so each score
 // costs half the matrix work but the same vector work (scaling, exp2,
 // normaliser, bf16 pack) as at d=128; the short rows of an image model add a
 // prologue and a masked last tile per handful of tiles.  Software pipelining
-// inside a wave needs two score buffers (182 VGPRs, two waves per SIMD);
-// running each wave's tiles one after another needs 140, so three
-// workgroups share a CU and the SIMDs overlap one wave's matrix work with
-// another's vector work instead.  Measured side by side against the
-// pipelined kernel at d=64, identical results: B=64 H=12 N=196 0.0280 ->
-// 0.0233 ms (0.0257 -> 0.0212 causal); N=512 to 8192, causal or not, 2-7 %
-// faster.  A wave also skips the second 32-key block of a tile (its score
-// and P V products and exponentials) when every key in it is masked for all
-// its rows: the last tile of a 196-key row holds 4 keys.
+// inside a wave needs two score buffers (182 VGPRs at d=64, two waves per
+// SIMD); running each wave's tiles one after another needs 146, so three
+// four-wave workgroups share a CU and the SIMDs overlap one wave's matrix
+// work with another's vector work instead.  Measured side by side against
+// the pipelined kernel at d=64, identical results: B=64 H=12 N=196 0.0280
+// -> 0.0233 ms (0.0257 -> 0.0212 causal); N=512 to 8192, causal or not, 2-7
+// % faster.  At d=128 (239 VGPRs, two workgroups per CU) it wins only on
+// short rows (launch_mfma_bf16).  A wave also skips the second 32-key block
+// of a tile (its score and P V products and exponentials) when every key in
+// it is masked for all its rows: the last tile of a 196-key row holds 4 keys.
 
 template <int D>
 __global__ void __launch_bounds__(256, D == 64 ? 3 : 2)
