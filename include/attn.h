@@ -128,8 +128,9 @@ int attn_fp8_prepare(const float* q, const float* k, const float* v,
  * MFMA: each e4m3 V operand is widened to fp16 (exact) in registers, and P,
  * carrying the V tile's scale relative to the head's largest V tile scale,
  * is rounded to fp16 (nearest-even).  o is bf16
- * [B][H][N][d]; lse (nullable) float32 [B][H][N].  Other conventions as
- * attn_fwd.
+ * [B][H][N][d]; lse (nullable) float32 [B][H][N].  The tile scales must be
+ * positive normal floats, as attn_fp8_prepare writes them; they live in
+ * device memory and are not checked.  Other conventions as attn_fwd.
  */
 int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  const float* q_scale, const float* k_scale,

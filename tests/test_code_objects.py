@@ -24,7 +24,7 @@ QUOTED = {
     "attn_mfma_bf16_kernelILi128ELi8E": (239, 65536),
     "attn_mfma_bf16_seq_kernelILi64E": (146, 32768),
     "attn_mfma_bf16_seq_kernelILi128E": (239, 65536),
-    "attn_fp8_kernelILi128ELb0E": (161, 32768),
+    "attn_fp8_kernelILi128ELb0E": (165, 32768),
     "bwd_dkdv_kernelILi128ELi8E": (246, 132096),
     "bwd_dq_kernelILi128ELi8E": (256, 98304),
 }
@@ -74,10 +74,12 @@ def test_eight_wave_kernels_fit_two_waves_per_simd():
             assert k["lds"] <= 160 * 1024, k
 
 
-def test_d64_forward_fits_three_workgroups_per_cu():
-    # the one-tile-at-a-time d=64 kernel relies on three four-wave workgroups
-    # per CU: at most 168 VGPRs (8-register granule) and a third of the LDS
-    hit = [k for k in _kernels() if "attn_mfma_bf16_seq_kernelILi64E" in k["name"]]
+@pytest.mark.parametrize("frag", ["attn_mfma_bf16_seq_kernelILi64E", "attn_fp8_kernelI"])
+def test_four_wave_forwards_fit_three_workgroups_per_cu(frag):
+    # the one-tile-at-a-time d=64 kernel and the fp8 forward rely on three
+    # four-wave workgroups per CU: at most 168 VGPRs (8-register granule) and
+    # a third of the LDS
+    hit = [k for k in _kernels() if frag in k["name"]]
     assert hit
     for k in hit:
         assert -(-k["vgpr"] // 8) * 8 + k["agpr"] <= 168, k
