@@ -340,6 +340,10 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
         }
       lsum += (ls0 + ls1) * rsv;
       // ---- O^T += V^T P'^T on fp16 ----
+      // The wave raises its issue priority for its P V products, so that of
+      // the three waves sharing a SIMD the one with matrix work ready goes
+      // first (1-2 % faster than equal priorities).
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c16 = 0; c16 < 4; ++c16) {
         const u32x4 pwv = u32x4{pw[c16][0], pw[c16][1], pw[c16][2], pw[c16][3]};
@@ -356,6 +360,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (t + 1 < ntiles) wait_vmcnt<0>();          // this wave's copies of tile t+1 landed
     __syncthreads();
   }
