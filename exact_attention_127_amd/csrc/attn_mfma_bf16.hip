@@ -520,28 +520,66 @@ __device__ __forceinline__ void load_q(WaveState<D>& w, const uint16_t* q, int64
   }
 }
 
-// Epilogue: the deferred division by the normaliser, bf16 O, natural-log LSE.
+// The wave's 32 Q rows copied into an LDS region laid out like the first 32
+// rows of a K tile (same swizzle): one 1 KB block of whole rows per copy
+// instruction, where loading the B operands from global memory directly
+// takes 32-byte pieces of 32 rows per instruction.  Rows past the end read
+// as zero.  dst: the region's LDS byte address (wave-uniform).
 template <int D>
-__device__ __forceinline__ void store_rows(const WaveState<D>& w, uint16_t* o, float* lse, int64_t base,
-                                           int bh, int N, int qrow, int h) {
-  const float ltot = halves_sum(w.lsum);
-  if (qrow < N) {
-    const float inv = 1.f / ltot;
-    uint16_t* orow = o + base + static_cast<int64_t>(qrow) * D;
+__device__ __forceinline__ void issue_q_copy(uint32_t dst, const uint16_t* q, int64_t base, int q0w, int N,
+                                             int lane) {
+  using C = Cfg<D, 4>;
+  constexpr int NB = BRW * C::ROWB / 1024;
+  const int rows = max(0, min(BRW, N - q0w));
+  i32x4 desc = buffer_desc(q + base + static_cast<int64_t>(min(q0w, N)) * D,
+                           static_cast<uint32_t>(rows) * C::ROWB);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int k = 0; k < 4; ++k) desc[k] = __builtin_amdgcn_readfirstlane(desc[k]);   // wave-uniform
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = db * 32 + 8 * g + 4 * h;
-        u32x2 wv;
-        wv[0] = pack_bf16x2(w.oacc[db][4 * g + 0] * inv, w.oacc[db][4 * g + 1] * inv);
-        wv[1] = pack_bf16x2(w.oacc[db][4 * g + 2] * inv, w.oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + col) = wv;
-      }
-    if (lse != nullptr && h == 0)
-      lse[static_cast<int64_t>(bh) * N + qrow] = (w.m + __log2f(ltot)) * kLn2;
+  for (int b = 0; b < NB; ++b) {
+    const int row = b * C::RPB + lane / C::CPR;
+    const int pos = lane % C::CPR;
+    dma16(desc, dst + static_cast<uint32_t>(b * 1024), row * C::ROWB + ((pos ^ kswz<D>(row)) << 4));
   }
 }
+
+// Epilogue through LDS.  The wave's 32 rows of bf16 O go to its own LDS
+// region (rows of 2D bytes, 16-byte chunks swizzled by the row so that the
+// 8-byte writes of one instruction spread over the banks), then come back
+// in row order: each global store instruction writes whole rows, 64 lanes x
+// 16 contiguous bytes, instead of 16-byte pieces of 32 rows.  The region
+// must not be in use by another wave (callers pass K/V ring space after the
+// loop's last barrier).
+template <int D>
+__device__ __forceinline__ void store_rows_lds(const WaveState<D>& w, char* stage, uint16_t* o, float* lse,
+                                               int64_t base, int bh, int N, int q0w, int j, int h, int lane) {
+  constexpr int RB = 2 * D;                 // bytes per row
+  constexpr int CPR = RB / 16;              // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;             // rows per store instruction
+  const float ltot = halves_sum(w.lsum);
+  const float inv = 1.f / ltot;
+  char* row = stage + j * RB;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = db * 4 + g;             // chunk of channels 8c..8c+7; the lane holds 8c + 4h .. +3
+      u32x2 wv;
+      wv[0] = pack_bf16x2(w.oacc[db][4 * g + 0] * inv, w.oacc[db][4 * g + 1] * inv);
+      wv[1] = pack_bf16x2(w.oacc[db][4 * g + 2] * inv, w.oacc[db][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2*>(row + ((c ^ (j % CPR)) << 4) + 8 * h) = wv;
+    }
+  if (lse != nullptr && h == 0 && q0w + j < N)
+    lse[static_cast<int64_t>(bh) * N + q0w + j] = (w.m + __log2f(ltot)) * kLn2;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * RB + ((c ^ (r % CPR)) << 4));
+    if (q0w + r < N)
+      *reinterpret_cast<u32x4*>(o + base + static_cast<int64_t>(q0w + r) * D + c * 8) = x;
+  }
+}
+
 // ---- one tile at a time (the d=64 kernel; the last tile of a pipelined wave) ----
 constexpr int kSeqReadAhead = 3;   // LDS operands in flight
 
@@ -775,7 +813,10 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (t + 1 < ntiles) iteration(t + 1, sb, sa, peb, pea, leb, lea);
   }
 
-  store_rows<D>(w, o, lse, base, bh, N, qrow, h);
+  // the rings are free after the last barrier: waves 0-3 stage O in the K
+  // ring, waves 4-7 in the V ring (32 rows x 2D bytes each)
+  static_assert(NW <= 8 && 4 * BRW * 2 * D <= 2 * C::TILEB, "O staging fits the rings");
+  store_rows_lds<D>(w, (wave < 4 ? kring : vring) + (wave & 3) * BRW * 2 * D, o, lse, base, bh, N, q0w, j, h, lane);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -802,12 +843,12 @@ hipError_t launch_one(const LaunchArgs& a) {
 // normaliser, bf16 pack) as at d=128; the short rows of an image model add a
 // prologue and a masked last tile per handful of tiles.  Software pipelining
 // inside a wave needs two score buffers (182 VGPRs at d=64, two waves per
-// SIMD); running each wave's tiles one after another needs 146, so three
+// SIMD); running each wave's tiles one after another needs 156, so three
 // four-wave workgroups share a CU and the SIMDs overlap one wave's matrix
 // work with another's vector work instead.  Measured side by side against
 // the pipelined kernel at d=64, identical results: B=64 H=12 N=196 0.0280
 // -> 0.0233 ms (0.0257 -> 0.0212 causal); N=512 to 8192, causal or not, 2-7
-// % faster.  At d=128 (239 VGPRs, two workgroups per CU) it wins only on
+// % faster.  At d=128 (256 VGPRs, two workgroups per CU) it wins only on
 // short rows (launch_mfma_bf16).  A wave also skips the second 32-key block
 // of a tile (its score and P V products and exponentials) when every key in
 // it is masked for all its rows: the last tile of a 196-key row holds 4 keys.
@@ -866,9 +907,16 @@ attn_mfma_bf16_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __rest
   const uint32_t kring_a = lds_addr(kring), vring_a = lds_addr(vring);
   issue_copy<D, NW, false>(kring_a, kbase, 0, N, wave, lane);
   issue_copy<D, NW, true>(vring_a, vbase, 0, N, wave, lane);
-  load_q<D>(w, q, base, q0w, N, j, h);
+  // Q through the second ring slots (free until the first iteration's
+  // copies): waves 0-1 in the K slot, waves 2-3 in the V slot, 32 rows each
+  static_assert(2 * BRW * C::ROWB == C::TILEB, "two waves' Q rows fill a slot");
+  const int qoff = C::TILEB + (wave & 1) * (BRW * C::ROWB);
+  const char* qst = (wave < 2 ? kring : vring) + qoff;
+  issue_q_copy<D>((wave < 2 ? kring_a : vring_a) + qoff, q, base, q0w, N, lane);
   wait_vmcnt<0>();
-  __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) w.qr[ks] = *reinterpret_cast<const bf16x8*>(qst + la.kofs[ks]);
+  __syncthreads();   // K0/V0 landed for every wave; every wave holds its Q before slot 1 is refilled
 
   // At the top of iteration t, K and V of tile t are in ring slot t&1; the
   // iteration copies tile t+1 into the other slot, which every wave left at
@@ -892,7 +940,8 @@ attn_mfma_bf16_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __rest
     __syncthreads();
   }
 
-  store_rows<D>(w, o, lse, base, bh, N, qrow, h);
+  static_assert(NW * BRW * 2 * D <= 4 * C::TILEB, "O staging fits the rings");
+  store_rows_lds<D>(w, smem + wave * BRW * 2 * D, o, lse, base, bh, N, q0w, j, h, lane);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

@@ -21,9 +21,9 @@ LLVM = "/opt/rocm/llvm/bin"
 
 # kernel (demangled-name fragment) -> (VGPRs, LDS bytes) as quoted in the design notes
 QUOTED = {
-    "attn_mfma_bf16_kernelILi128ELi8E": (239, 65536),
-    "attn_mfma_bf16_seq_kernelILi64E": (146, 32768),
-    "attn_mfma_bf16_seq_kernelILi128E": (239, 65536),
+    "attn_mfma_bf16_kernelILi128ELi8E": (251, 65536),
+    "attn_mfma_bf16_seq_kernelILi64E": (156, 32768),
+    "attn_mfma_bf16_seq_kernelILi128E": (256, 65536),
     "attn_fp8_kernelILi128ELb0E": (152, 32768),
     "bwd_dkdv_kernelILi128ELi8E": (246, 132096),
     "bwd_dq_kernelILi128ELi8E": (256, 98304),
