@@ -172,26 +172,37 @@ __device__ __forceinline__ void update_reference(const f32x16 (&sacc)[2], float 
   }
 }
 
-// Epilogue: O = acc * oscale / l in bf16, LSE in natural log.
+// Epilogue: O = acc * oscale / l in bf16, LSE in natural log.  The wave's
+// 32 bf16 rows go through its own LDS region (rows of 2D bytes, 16-byte
+// chunks swizzled by the row) and are stored in row order, each store
+// instruction writing whole rows (1 KB contiguous) instead of 8-byte pieces
+// of 32 rows.  The region must be idle (ring space after the last barrier).
 template <int D>
 __device__ __forceinline__ void store_rows8(const f32x16 (&oacc)[D / 32], float m, float lsum, float oscale,
-                                            uint16_t* o, float* lse, int64_t base, int bh, int N, int qrow, int h) {
+                                            char* stage, uint16_t* o, float* lse, int64_t base, int bh, int N,
+                                            int q0w, int j, int h, int lane) {
+  constexpr int RB = 2 * D, CPR = RB / 16, RPI = 64 / CPR;
   const float ltot = halves_sum(lsum);
-  if (qrow < N) {
-    const float inv = oscale / ltot;
-    uint16_t* orow = o + base + static_cast<int64_t>(qrow) * D;
+  const float inv = oscale / ltot;
+  char* row = stage + j * RB;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = db * 32 + 8 * g + 4 * h;
-        u32x2 wv;
-        wv[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        wv[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + col) = wv;
-      }
-    if (lse != nullptr && h == 0)
-      lse[static_cast<int64_t>(bh) * N + qrow] = (m + __log2f(ltot)) * kLn2;
+    for (int g = 0; g < 4; ++g) {
+      const int c = db * 4 + g;             // chunk of channels 8c..8c+7; the lane holds 8c + 4h .. +3
+      u32x2 wv;
+      wv[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+      wv[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2*>(row + ((c ^ (j % CPR)) << 4) + 8 * h) = wv;
+    }
+  if (lse != nullptr && h == 0 && q0w + j < N)
+    lse[static_cast<int64_t>(bh) * N + q0w + j] = (m + __log2f(ltot)) * kLn2;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * RB + ((c ^ (r % CPR)) << 4));
+    if (q0w + r < N)
+      *reinterpret_cast<u32x4*>(o + base + static_cast<int64_t>(q0w + r) * D + c * 8) = x;
   }
 }
 #endif
@@ -365,7 +376,10 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
     __syncthreads();
   }
 
-  store_rows8<D>(oacc, m, lsum, svmax, o, lse, base, bh, N, qrow, h);
+  // waves 0-1 stage O in the K ring, waves 2-3 in the V ring
+  static_assert(2 * 32 * 2 * D <= 2 * C::TILEB, "O staging fits the rings");
+  store_rows8<D>(oacc, m, lsum, svmax, (wave < 2 ? kring : vring) + (wave & 1) * (32 * 2 * D), o, lse, base, bh,
+                 N, q0w, j, h, lane);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -596,7 +610,9 @@ attn_mxfp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8
     __syncthreads();
   }
 
-  store_rows8<D>(oacc, m, lsum, 1.f, o, lse, base, bh, N, qrow, h);
+  // the bf16 V ring holds the four waves' staged O
+  static_assert(4 * 32 * 2 * D <= 2 * C::TILEB16, "O staging fits the V ring");
+  store_rows8<D>(oacc, m, lsum, 1.f, vring + wave * (32 * 2 * D), o, lse, base, bh, N, q0w, j, h, lane);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
