@@ -161,6 +161,36 @@ __device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc
       *reinterpret_cast<u32x2*>(out_row + db * 32 + 8 * g + 4 * h) = wv;
     }
 }
+
+// The same block through LDS: the wave's 32 rows r0 .. r0+31 go to its own
+// idle LDS region `stage` (rows of 2D bytes, 16-byte chunks swizzled by the
+// row so that one instruction's 8-byte writes spread over the banks) and
+// are stored in row order, each store instruction writing whole rows (1 KB
+// contiguous) instead of 8-byte pieces of 32 rows.  Rows at or past N are
+// not stored.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(uint16_t* out, int r0, int N, const f32x16 (&acc)[D / 32],
+                                               float mul, char* stage, int j, int h, int lane) {
+  constexpr int RB = 2 * D, CPR = RB / 16, RPI = 64 / CPR;
+  char* row = stage + j * RB;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = db * 4 + g;             // chunk of channels 8c..8c+7; the lane holds 8c + 4h .. +3
+      u32x2 wv;
+      wv[0] = pack_bf16x2(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
+      wv[1] = pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+      *reinterpret_cast<u32x2*>(row + ((c ^ (j % CPR)) << 4) + 8 * h) = wv;
+    }
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * RB + ((c ^ (r % CPR)) << 4));
+    if (r0 + r < N)
+      *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(r0 + r) * D + c * 8) = x;
+  }
+}
 #endif  // __HIP_DEVICE_COMPILE__
 
 // ---- D_i = sum_c dO_ic O_ic, float32, one row per D/8 lanes ----
@@ -378,6 +408,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int r = (ntiles - 1) % 3;
     phase(2 * ntiles - 1, std::integral_constant<int, 1>{}, so, dpo, se, dpe, kslot(r), kslot(r), vslot(r));
   }
+  // (staging dQ through LDS as dK/dV do costs this 256-VGPR kernel spills)
   if (qrow < N) store_rows<D>(dq + base + static_cast<int64_t>(qrow) * D, acc, h, scale);
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -547,10 +578,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (qt + 1 < nqt) lse_to_base2(slot ^ 1);
     __syncthreads();
   }
-  if (key < N) {
-    store_rows<D>(dk + base + static_cast<int64_t>(key) * D, dka, h, scale);
-    store_rows<D>(dv + base + static_cast<int64_t>(key) * D, dva, h, 1.f);
-  }
+  // the loop's last barrier left the LDS idle: each wave stages dK, then dV,
+  // in its own 32-row region
+  static_assert(NW * 32 * 2 * D <= static_cast<int>(sizeof(smem)), "dK/dV staging fits the LDS");
+  char* stage = smem + wave * (32 * 2 * D);
+  store_rows_lds<D>(dk + base, k0w, N, dka, scale, stage, j, h, lane);
+  store_rows_lds<D>(dv + base, k0w, N, dva, 1.f, stage, j, h, lane);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
