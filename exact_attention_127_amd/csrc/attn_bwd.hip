@@ -183,12 +183,15 @@ __device__ __forceinline__ void store_rows_lds(uint16_t* out, int r0, int N, con
       wv[1] = pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
       *reinterpret_cast<u32x2*>(row + ((c ^ (j % CPR)) << 4) + 8 * h) = wv;
     }
+  // stores through a descriptor that covers the valid rows only: rows at or
+  // past N are dropped by its range check, without a branch
+  const int rows = max(0, min(32, N - r0));
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(out + static_cast<int64_t>(min(r0, N)) * D, 0, rows * RB, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, c = lane % CPR;
     const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * RB + ((c ^ (r % CPR)) << 4));
-    if (r0 + r < N)
-      *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(r0 + r) * D + c * 8) = x;
+    __builtin_amdgcn_raw_buffer_store_b128(x, rs, r * RB + c * 16, 0, 0);
   }
 }
 #endif  // __HIP_DEVICE_COMPILE__

@@ -197,12 +197,15 @@ __device__ __forceinline__ void store_rows8(const f32x16 (&oacc)[D / 32], float 
     }
   if (lse != nullptr && h == 0 && q0w + j < N)
     lse[static_cast<int64_t>(bh) * N + q0w + j] = (m + __log2f(ltot)) * kLn2;
+  // stores through a descriptor that covers the valid rows only: rows at or
+  // past N are dropped by its range check, without a branch
+  const int rows = max(0, min(32, N - q0w));
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(o + base + static_cast<int64_t>(min(q0w, N)) * D, 0, rows * RB, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, c = lane % CPR;
     const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * RB + ((c ^ (r % CPR)) << 4));
-    if (q0w + r < N)
-      *reinterpret_cast<u32x4*>(o + base + static_cast<int64_t>(q0w + r) * D + c * 8) = x;
+    __builtin_amdgcn_raw_buffer_store_b128(x, rs, r * RB + c * 16, 0, 0);
   }
 }
 #endif
