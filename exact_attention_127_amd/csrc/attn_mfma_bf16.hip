@@ -783,7 +783,13 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (t < last) {
       const int kv0n = (t + 1) * BC;
       float ll;
+      // Issue priority alternates between the two waves of a SIMD (w and
+      // w+4): waves 0-3 lead the score phase, waves 4-7 the P V phase.
+      // Measured 0.3-0.7 % faster than equal priorities on every shape tried
+      // (16k 0.9018 -> 0.8954 ms); the reversed assignment gains nothing.
+      if (wave < 4) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
       phase_a<D>(w, snext, pb, ll, scur, la, kst_next);
+      if (wave < 4) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
       commit_tile<D>(w, scur, pb, pecur, lecur, ll);
       const bool mask_next = (causal && kv0n + BC - 1 > q0w) || (kv0n + BC > N);
       if (mask_next) apply_mask(snext, kv0n, N, qrow, h, causal);
