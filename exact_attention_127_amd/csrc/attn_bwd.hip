@@ -185,8 +185,14 @@ __device__ __forceinline__ void store_rows_lds(uint16_t* out, int r0, int N, con
     }
   // stores through a descriptor that covers the valid rows only: rows at or
   // past N are dropped by its range check, without a branch
-  const int rows = max(0, min(32, N - r0));
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(out + static_cast<int64_t>(min(r0, N)) * D, 0, rows * RB, 0x00020000);
+  // the wave's first row is wave-uniform; saying so keeps the descriptor in
+  // scalar registers (a vector-held one makes the compiler loop over lanes)
+  const int r0u = __builtin_amdgcn_readfirstlane(r0);
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, N - r0u)));
+  const uint64_t pa = reinterpret_cast<uint64_t>(out + static_cast<int64_t>(min(r0u, N)) * D);
+  const uint64_t pu = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32))) << 32) |
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa)));
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0, rows * RB, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, c = lane % CPR;

@@ -199,8 +199,14 @@ __device__ __forceinline__ void store_rows8(const f32x16 (&oacc)[D / 32], float 
     lse[static_cast<int64_t>(bh) * N + q0w + j] = (m + __log2f(ltot)) * kLn2;
   // stores through a descriptor that covers the valid rows only: rows at or
   // past N are dropped by its range check, without a branch
-  const int rows = max(0, min(32, N - q0w));
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(o + base + static_cast<int64_t>(min(q0w, N)) * D, 0, rows * RB, 0x00020000);
+  // the wave's first row is wave-uniform; saying so keeps the descriptor in
+  // scalar registers (a vector-held one makes the compiler loop over lanes)
+  const int r0u = __builtin_amdgcn_readfirstlane(q0w);
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, N - r0u)));
+  const uint64_t pa = reinterpret_cast<uint64_t>(o + base + static_cast<int64_t>(min(r0u, N)) * D);
+  const uint64_t pu = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32))) << 32) |
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa)));
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0, rows * RB, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, c = lane % CPR;

@@ -504,27 +504,12 @@ __device__ __forceinline__ void work_item(int id, int BH, int nqb, bool causal, 
   }
 }
 
-// The wave's 32 query rows as the B operand of the score products (rows
-// past N read as zero through the buffer bounds).
-template <int D>
-__device__ __forceinline__ void load_q(WaveState<D>& w, const uint16_t* q, int64_t base, int q0w, int N,
-                                       int j, int h) {
-  const int rows = max(0, min(BRW, N - q0w));
-  const auto rq = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(q + base + static_cast<int64_t>(min(q0w, N)) * D), 0,
-      static_cast<int>(rows * 2 * D), 0x00020000);
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, j * 2 * D + (ks * 16 + 8 * h) * 2, 0, 0);
-    w.qr[ks] = __builtin_bit_cast(bf16x8, x);
-  }
-}
-
-// The wave's 32 Q rows copied into an LDS region laid out like the first 32
-// rows of a K tile (same swizzle): one 1 KB block of whole rows per copy
-// instruction, where loading the B operands from global memory directly
-// takes 32-byte pieces of 32 rows per instruction.  Rows past the end read
-// as zero.  dst: the region's LDS byte address (wave-uniform).
+// The wave's 32 Q rows (the B operands of the score products) copied into
+// an LDS region laid out like the first 32 rows of a K tile (same
+// swizzle): one 1 KB block of whole rows per copy instruction, where
+// loading the operands from global memory directly takes 32-byte pieces of
+// 32 rows per instruction.  Rows past the end read as zero.  dst: the
+// region's LDS byte address (wave-uniform).
 template <int D>
 __device__ __forceinline__ void issue_q_copy(uint32_t dst, const uint16_t* q, int64_t base, int q0w, int N,
                                              int lane) {
@@ -573,8 +558,14 @@ __device__ __forceinline__ void store_rows_lds(const WaveState<D>& w, char* stag
     lse[static_cast<int64_t>(bh) * N + q0w + j] = (w.m + __log2f(ltot)) * kLn2;
   // stores through a descriptor that covers the valid rows only: rows at or
   // past N are dropped by its range check, without a branch
-  const int rows = max(0, min(32, N - q0w));
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(o + base + static_cast<int64_t>(min(q0w, N)) * D, 0, rows * RB, 0x00020000);
+  // the wave's first row is wave-uniform; saying so keeps the descriptor in
+  // scalar registers (a vector-held one makes the compiler loop over lanes)
+  const int r0u = __builtin_amdgcn_readfirstlane(q0w);
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, N - r0u)));
+  const uint64_t pa = reinterpret_cast<uint64_t>(o + base + static_cast<int64_t>(min(r0u, N)) * D);
+  const uint64_t pu = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32))) << 32) |
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa)));
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0, rows * RB, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, c = lane % CPR;
@@ -712,6 +703,9 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILEB];
   char* const kring = smem;
   char* const vring = smem + 2 * C::TILEB;
+  // Q staging: the registers already limit a CU to one workgroup, so these
+  // 64 KB of LDS are otherwise unused
+  __shared__ __attribute__((aligned(1024))) char qstage[NW * BRW * C::ROWB];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -749,13 +743,17 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   if (q0w < N) last = causal ? min(ntiles - 1, (q0w + BRW - 1) / BC) : ntiles - 1;
   const int kmax = causal ? min(N - 1, q0w + BRW - 1) : N - 1;
 
-  // ---- prologue: K0, V0, K1 and Q in flight; scores of tile 0 ----
+  // ---- prologue: K0, V0, K1 and Q in flight (Q copied through LDS in whole
+  // rows, then read as operands); scores of tile 0 ----
   const uint32_t kring_a = lds_addr(kring), vring_a = lds_addr(vring);   // LDS byte addresses
   issue_copy<D, NW, false>(kring_a, kbase, 0, N, wave, lane);
   issue_copy<D, NW, true>(vring_a, vbase, 0, N, wave, lane);
   if (ntiles > 1) issue_copy<D, NW, false>(kring_a + C::TILEB, kbase, BC, N, wave, lane);
-  load_q<D>(w, q, base, q0w, N, j, h);
+  const char* qst = qstage + wave * (BRW * C::ROWB);
+  issue_q_copy<D>(lds_addr(qst), q, base, q0w, N, lane);
   wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) w.qr[ks] = *reinterpret_cast<const bf16x8*>(qst + la.kofs[ks]);
   __syncthreads();
 
   f32x16 sa[BC / 32], sb[BC / 32];   // scores of the current and the next tile
