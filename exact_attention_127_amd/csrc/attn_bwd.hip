@@ -185,14 +185,9 @@ __device__ __forceinline__ void store_rows_lds(uint16_t* out, int r0, int N, con
     }
   // stores through a descriptor that covers the valid rows only: rows at or
   // past N are dropped by its range check, without a branch
-  // the wave's first row is wave-uniform; saying so keeps the descriptor in
-  // scalar registers (a vector-held one makes the compiler loop over lanes)
   const int r0u = __builtin_amdgcn_readfirstlane(r0);
-  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, N - r0u)));
-  const uint64_t pa = reinterpret_cast<uint64_t>(out + static_cast<int64_t>(min(r0u, N)) * D);
-  const uint64_t pu = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32))) << 32) |
-                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa)));
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0, rows * RB, 0x00020000);
+  const int rows = max(0, min(32, N - r0u));
+  const auto rs = uniform_rsrc(out + static_cast<int64_t>(min(r0u, N)) * D, rows * RB);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, c = lane % CPR;
@@ -295,8 +290,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   {
     const int rows = max(0, min(32, N - q0w));
     const int64_t r0 = base + static_cast<int64_t>(min(q0w, N)) * D;
-    const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(q + r0), 0, rows * T::ROWB, 0x00020000);
-    const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dout + r0), 0, rows * T::ROWB, 0x00020000);
+    const auto rq = uniform_rsrc(q + r0, rows * T::ROWB);
+    const auto rd = uniform_rsrc(dout + r0, rows * T::ROWB);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const int off = j * T::ROWB + (ks * 16 + 8 * h) * 2;
@@ -442,7 +437,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   char* const qring = smem + VB;
   char* const dring = qring + 2 * T::TILEB;
   char* const sring = dring + 2 * T::TILEB;    // [slot][LSE BT floats | D BT floats]
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, j = lane & 31, h = lane >> 5;
 
   // work item: whole heads per XCD; causal: the first key blocks see the
   // most query tiles, so they go first
@@ -478,7 +473,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   {
     const int rows = max(0, min(32, N - k0w));
     const int64_t r0 = base + static_cast<int64_t>(min(k0w, N)) * D;
-    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + r0), 0, rows * T::ROWB, 0x00020000);
+    const auto rk = uniform_rsrc(k + r0, rows * T::ROWB);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const int off = j * T::ROWB + (ks * 16 + 8 * h) * 2;

@@ -199,14 +199,9 @@ __device__ __forceinline__ void store_rows8(const f32x16 (&oacc)[D / 32], float 
     lse[static_cast<int64_t>(bh) * N + q0w + j] = (m + __log2f(ltot)) * kLn2;
   // stores through a descriptor that covers the valid rows only: rows at or
   // past N are dropped by its range check, without a branch
-  // the wave's first row is wave-uniform; saying so keeps the descriptor in
-  // scalar registers (a vector-held one makes the compiler loop over lanes)
   const int r0u = __builtin_amdgcn_readfirstlane(q0w);
-  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, N - r0u)));
-  const uint64_t pa = reinterpret_cast<uint64_t>(o + base + static_cast<int64_t>(min(r0u, N)) * D);
-  const uint64_t pu = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32))) << 32) |
-                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa)));
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0, rows * RB, 0x00020000);
+  const int rows = max(0, min(32, N - r0u));
+  const auto rs = uniform_rsrc(o + base + static_cast<int64_t>(min(r0u, N)) * D, rows * RB);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, c = lane % CPR;
@@ -236,7 +231,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   __shared__ __attribute__((aligned(1024))) char vring[2 * C::TILEB];     // e4m3 V, two slots
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int j = lane & 31;
   const int h = lane >> 5;
@@ -267,8 +262,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
   i32x8 qr[D / 64];
   {
     const int rows = max(0, min(32, N - q0w));
-    const auto rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(q8 + base + static_cast<int64_t>(min(q0w, N)) * D), 0, rows * D, 0x00020000);
+    const auto rq = uniform_rsrc(q8 + base + static_cast<int64_t>(min(q0w, N)) * D, rows * D);
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks) {
       const int lo_c = ks * 64 + 32 * h;
@@ -462,7 +456,7 @@ attn_mxfp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8
   __shared__ __attribute__((aligned(1024))) char vring[2 * C::TILEB16];   // bf16 V, two slots
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int j = lane & 31;
   const int h = lane >> 5;
@@ -521,8 +515,7 @@ attn_mxfp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8
   i32x8 qr[D / 64];
   {
     const int rows = max(0, min(32, N - q0w));
-    const auto rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(q8 + base + static_cast<int64_t>(min(q0w, N)) * D), 0, rows * D, 0x00020000);
+    const auto rq = uniform_rsrc(q8 + base + static_cast<int64_t>(min(q0w, N)) * D, rows * D);
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks)
       qr[ks] = join8(__builtin_amdgcn_raw_buffer_load_b128(rq, j * D + ks * 64 + 16 * h, 0, 0),

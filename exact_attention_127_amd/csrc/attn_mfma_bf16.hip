@@ -558,14 +558,9 @@ __device__ __forceinline__ void store_rows_lds(const WaveState<D>& w, char* stag
     lse[static_cast<int64_t>(bh) * N + q0w + j] = (w.m + __log2f(ltot)) * kLn2;
   // stores through a descriptor that covers the valid rows only: rows at or
   // past N are dropped by its range check, without a branch
-  // the wave's first row is wave-uniform; saying so keeps the descriptor in
-  // scalar registers (a vector-held one makes the compiler loop over lanes)
   const int r0u = __builtin_amdgcn_readfirstlane(q0w);
-  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, N - r0u)));
-  const uint64_t pa = reinterpret_cast<uint64_t>(o + base + static_cast<int64_t>(min(r0u, N)) * D);
-  const uint64_t pu = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa >> 32))) << 32) |
-                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pa)));
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0, rows * RB, 0x00020000);
+  const int rows = max(0, min(32, N - r0u));
+  const auto rs = uniform_rsrc(o + base + static_cast<int64_t>(min(r0u, N)) * D, rows * RB);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, c = lane % CPR;
@@ -781,13 +776,14 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (t < last) {
       const int kv0n = (t + 1) * BC;
       float ll;
-      // Issue priority alternates between the two waves of a SIMD (w and
-      // w+4): waves 0-3 lead the score phase, waves 4-7 the P V phase.
-      // Measured 0.3-0.7 % faster than equal priorities on every shape tried
-      // (16k 0.9018 -> 0.8954 ms); the reversed assignment gains nothing.
-      if (wave < 4) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+      // A wave issues its score phase at raised priority and its P V phase
+      // at the normal one, so when the two waves of a SIMD drift apart the
+      // one starting a tile's score products goes first: 0.3-0.7 % faster
+      // than equal priorities on every shape tried (16k 0.9018 -> 0.8954
+      // ms); raising the P V phase instead gains nothing.
+      __builtin_amdgcn_s_setprio(1);
       phase_a<D>(w, snext, pb, ll, scur, la, kst_next);
-      if (wave < 4) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(0);
       commit_tile<D>(w, scur, pb, pecur, lecur, ll);
       const bool mask_next = (causal && kv0n + BC - 1 > q0w) || (kv0n + BC > N);
       if (mask_next) apply_mask(snext, kv0n, N, qrow, h, causal);

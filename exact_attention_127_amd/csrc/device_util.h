@@ -28,6 +28,19 @@ __device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
                static_cast<int>(bytes), 0x00020000};
 }
 
+// Buffer resource for a wave-uniform range [base, base + bytes): base and
+// size go through readfirstlane, so the descriptor lives in scalar
+// registers (held in vector registers, it makes the compiler wrap every
+// access in a loop over the lanes' distinct descriptors).  Accesses at or
+// past `bytes` read zero and drop stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32))) << 32) |
+                     static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0, __builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+
 // 32-bit LDS byte address of a pointer into a __shared__ array, made
 // wave-uniform (an SGPR value).
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
