@@ -76,7 +76,7 @@ attn_simple_kernel(const T* __restrict__ q, const T* __restrict__ k,
   __shared__ __attribute__((aligned(16))) float smem[kSplit * C::PW];
   __shared__ float part_ml[kSplit][64][2];
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int quarter = lane % C::LPQ;     // which quarter of the row's channels
   const int nqb = (N + C::QPB - 1) / C::QPB;
