@@ -704,6 +704,7 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);   // the same value, known uniform
   const int lane = tid & 63;
   const int j = lane & 31;        // query column inside the wave's 32 rows
   const int h = lane >> 5;        // lane half
@@ -741,10 +742,10 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // ---- prologue: K0, V0, K1 and Q in flight (Q copied through LDS in whole
   // rows, then read as operands); scores of tile 0 ----
   const uint32_t kring_a = lds_addr(kring), vring_a = lds_addr(vring);   // LDS byte addresses
-  issue_copy<D, NW, false>(kring_a, kbase, 0, N, wave, lane);
-  issue_copy<D, NW, true>(vring_a, vbase, 0, N, wave, lane);
-  if (ntiles > 1) issue_copy<D, NW, false>(kring_a + C::TILEB, kbase, BC, N, wave, lane);
-  const char* qst = qstage + wave * (BRW * C::ROWB);
+  issue_copy<D, NW, false>(kring_a, kbase, 0, N, wave_u, lane);
+  issue_copy<D, NW, true>(vring_a, vbase, 0, N, wave_u, lane);
+  if (ntiles > 1) issue_copy<D, NW, false>(kring_a + C::TILEB, kbase, BC, N, wave_u, lane);
+  const char* qst = qstage + wave_u * (BRW * C::ROWB);
   issue_q_copy<D>(lds_addr(qst), q, base, q0w, N, lane);
   wait_vmcnt<0>();
 #pragma unroll
@@ -771,8 +772,8 @@ attn_mfma_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                        EarlyWords& penext, float& lecur, float& lenext) {
     const char* kst_next = kring + ((t + 1) & 1) * C::TILEB;
     const char* vst = vring + (t & 1) * C::TILEB;
-    if (t + 1 < ntiles) issue_copy<D, NW, true>(vring_a + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave, lane);
-    if (t + 2 < ntiles) issue_copy<D, NW, false>(kring_a + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave, lane);
+    if (t + 1 < ntiles) issue_copy<D, NW, true>(vring_a + ((t + 1) & 1) * C::TILEB, vbase, (t + 1) * BC, N, wave_u, lane);
+    if (t + 2 < ntiles) issue_copy<D, NW, false>(kring_a + (t & 1) * C::TILEB, kbase, (t + 2) * BC, N, wave_u, lane);
     if (t < last) {
       const int kv0n = (t + 1) * BC;
       float ll;

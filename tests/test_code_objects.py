@@ -21,7 +21,7 @@ LLVM = "/opt/rocm/llvm/bin"
 
 # kernel (demangled-name fragment) -> (VGPRs, LDS bytes) as quoted in the design notes
 QUOTED = {
-    "attn_mfma_bf16_kernelILi128ELi8E": (256, 131072),
+    "attn_mfma_bf16_kernelILi128ELi8E": (254, 131072),
     "attn_mfma_bf16_seq_kernelILi64E": (154, 32768),
     "attn_mfma_bf16_seq_kernelILi128E": (256, 65536),
     "attn_fp8_kernelILi128ELb0E": (152, 32768),
