@@ -145,24 +145,9 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Store a 32x32 accumulator block whose column is this lane's row `row` of
-// a [N][D] output and whose rows are channels 32db + 8g + 4h + (0..3),
-// multiplied by `mul`, as bf16.
-template <int D>
-__device__ __forceinline__ void store_rows(uint16_t* out_row, const f32x16 (&acc)[D / 32], int h,
-                                           float mul) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 wv;
-      wv[0] = pack_bf16x2(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
-      wv[1] = pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
-      *reinterpret_cast<u32x2*>(out_row + db * 32 + 8 * g + 4 * h) = wv;
-    }
-}
-
-// The same block through LDS: the wave's 32 rows r0 .. r0+31 go to its own
+// Store a 32x32 accumulator block (rows: channels 32db + 8g + 4h + 0..3;
+// columns: the wave's 32 rows r0 .. r0+31 of a [N][D] output), times `mul`,
+// as bf16 through LDS: the rows go to the wave's own
 // idle LDS region `stage` (rows of 2D bytes, 16-byte chunks swizzled by the
 // row so that one instruction's 8-byte writes spread over the banks) and
 // are stored in row order, each store instruction writing whole rows (1 KB
@@ -249,6 +234,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const bool causal = causal_arg != 0;
   __shared__ __attribute__((aligned(1024))) char smem[2 * kRingB * T::TILEB];   // K ring, then V ring
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);   // the same value, known uniform
 
   // work item: whole heads per XCD, heaviest causal query blocks first
   const int id = static_cast<int>(blockIdx.x);
@@ -282,8 +268,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   auto kslot = [&](int r) __attribute__((always_inline)) -> const char* { return smem + r * T::TILEB; };           // r = tile % 3
   auto vslot = [&](int r) __attribute__((always_inline)) -> const char* { return smem + (kRingB + r) * T::TILEB; };
   if (ntiles > 0) {
-    copy_tile<D, NW>(smem, kbase, 0, N, wave, lane);
-    copy_tile<D, NW>(smem + kRingB * T::TILEB, vbase, 0, N, wave, lane);
+    copy_tile<D, NW>(smem, kbase, 0, N, wave_u, lane);
+    copy_tile<D, NW>(smem + kRingB * T::TILEB, vbase, 0, N, wave_u, lane);
   }
   // this lane's Q and dO row as B operands (rows past N read as zero)
   bf16x8 qr[D / 16], dor[D / 16];
@@ -394,8 +380,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     constexpr int R = decltype(rc)::value;
     constexpr int RP = (R + 2) % 3, RN = (R + 1) % 3;
     if (t + 1 < ntiles) {
-      copy_tile<D, NW>(smem + RN * T::TILEB, kbase, (t + 1) * BT, N, wave, lane);
-      copy_tile<D, NW>(smem + (kRingB + RN) * T::TILEB, vbase, (t + 1) * BT, N, wave, lane);
+      copy_tile<D, NW>(smem + RN * T::TILEB, kbase, (t + 1) * BT, N, wave_u, lane);
+      copy_tile<D, NW>(smem + (kRingB + RN) * T::TILEB, vbase, (t + 1) * BT, N, wave_u, lane);
     }
     phase(2 * t - 1, std::integral_constant<int, 1>{}, so, dpo, se, dpe, kslot(RP), kslot(R), vslot(R));
     phase(2 * t, std::integral_constant<int, 0>{}, se, dpe, so, dpo, kslot(R), kslot(R), vslot(R));
@@ -412,8 +398,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int r = (ntiles - 1) % 3;
     phase(2 * ntiles - 1, std::integral_constant<int, 1>{}, so, dpo, se, dpe, kslot(r), kslot(r), vslot(r));
   }
-  // (staging dQ through LDS as dK/dV do costs this 256-VGPR kernel spills)
-  if (qrow < N) store_rows<D>(dq + base + static_cast<int64_t>(qrow) * D, acc, h, scale);
+  __syncthreads();   // every wave is done with the rings (the last block read its K tile)
+  static_assert(NW * 32 * 2 * D <= static_cast<int>(sizeof(smem)), "dQ staging fits the rings");
+  store_rows_lds<D>(dq + base, q0w, N, acc, scale, smem + wave_u * (32 * 2 * D), j, h, lane);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
