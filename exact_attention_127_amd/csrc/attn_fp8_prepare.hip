@@ -97,6 +97,20 @@ __device__ __forceinline__ void store_rotated_block(uint8_t* row, int ob, const 
 // MX = true: one E8M0 byte per 32 channels of each token (scale 2^e).
 // Work items are (tensor, batch*head, tile); the grid strides over them and
 // each wave loads its next tile's rows while it works on the current one.
+#if defined(__HIP_DEVICE_COMPILE__)
+// x / s rounded to nearest float32, from r = 1/s rounded to nearest: q =
+// x r is within an ulp of x/s, the remainder x - s q is exact in one fma,
+// and q + (x - s q) r rounds to the correctly rounded quotient (Markstein's
+// theorem; no overflow here, |x/s| <= 448, and quotients in the float32
+// subnormal range encode as e4m3 zero either way).  The sign is x's (s > 0):
+// for x = -0 the correction would otherwise produce +0.  Four vector
+// instructions where a division takes about ten.
+__device__ __forceinline__ float quot_rn(float x, float s, float r) {
+  const float q = x * r;
+  return copysignf(fmaf(fmaf(-s, q, x), r, q), x);
+}
+#endif
+
 template <int D, bool MX>
 __global__ void __launch_bounds__(kPrepThreads, 2)
 fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
@@ -208,14 +222,15 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
         for (int i = 1; i < kPrepWaves; ++i) am = fmaxf(am, red[par][i]);
         par ^= 1;
         const float sc = am > 0.f ? am / kE4m3Max : 1.f;
+        const float rsc = 1.f / sc;
         if (tid == 0) static_cast<float*>(scale_out)[static_cast<int64_t>(bh) * ntq + tile] = sc;
 #pragma unroll
         for (int ob = 0; ob < C::NB; ++ob) {
           uint32_t wd[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-            wd[g] = pack4_e4m3(acc[ob][4 * g] / sc, acc[ob][4 * g + 1] / sc,
-                               acc[ob][4 * g + 2] / sc, acc[ob][4 * g + 3] / sc);
+            wd[g] = pack4_e4m3(quot_rn(acc[ob][4 * g], sc, rsc), quot_rn(acc[ob][4 * g + 1], sc, rsc),
+                               quot_rn(acc[ob][4 * g + 2], sc, rsc), quot_rn(acc[ob][4 * g + 3], sc, rsc));
           store_rotated_block(dst, ob, wd, h, valid);
         }
       }
@@ -261,6 +276,7 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
         for (int i = 1; i < kPrepWaves; ++i) am = fmaxf(am, red[par][i]);
         par ^= 1;
         const float sc = am > 0.f ? am / kE4m3Max : 1.f;
+        const float rsc = 1.f / sc;
         if (tid == 0) static_cast<float*>(scale_out)[static_cast<int64_t>(bh) * ntq + tile] = sc;
 #pragma unroll
         for (int m = 0; m < C::NX / 4; ++m) {
@@ -268,7 +284,8 @@ fp8_prepare_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const f32x4 xv = x[4 * m + i];
-            cw[i] = pack4_e4m3(xv[0] / sc, xv[1] / sc, xv[2] / sc, xv[3] / sc);
+            cw[i] = pack4_e4m3(quot_rn(xv[0], sc, rsc), quot_rn(xv[1], sc, rsc), quot_rn(xv[2], sc, rsc),
+                               quot_rn(xv[3], sc, rsc));
           }
           if (valid) *reinterpret_cast<u32x4*>(out + 16 * m) = cw;
         }

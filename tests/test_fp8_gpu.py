@@ -83,6 +83,42 @@ def test_prepare_codec_edge_values(gpu):
     assert np.array_equal(v8, ov)
 
 
+@pytest.mark.parametrize("amax", [761.6, 1.0e-3, 3.0e5])
+def test_prepare_quotients_near_code_midpoints(gpu, amax):
+    """Values x whose quotient x/s lands on, or a few float32 ulps beside,
+    the midpoint between two adjacent e4m3 codes, for a scale s = amax/448
+    that is not a power of two: the codes follow the float32 quotient
+    rounded to nearest, as the oracle computes it."""
+    table = oracle.e4m3_table()
+    pos = table[:127]
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    am = np.float32(amax)
+    s = np.float32(am / np.float32(448.0))
+    vals = []
+    for m in mids:                         # x = fl(m s) and its neighbours up to 3 ulps away
+        x0 = np.float32(m * s)
+        up = dn = x0
+        vals.append(x0)
+        for _ in range(3):
+            up = np.nextafter(up, np.float32(np.inf))
+            dn = np.nextafter(dn, np.float32(-np.inf))
+            vals += [up, dn]
+    vals = np.asarray(vals, np.float32)
+    vals = np.concatenate([vals, -vals])
+    d = 64
+    N = 128 * (-(-(vals.size + 1) // (128 * d)))
+    v = np.zeros((1, 1, N, d), np.float32)
+    flat = v.reshape(-1)
+    flat[:vals.size] = vals
+    for t in range(N // 128):              # every tile's largest magnitude is amax
+        flat[t * 128 * d + 128 * d - 1] = am
+    inp = {"q": v.copy(), "k": v.copy(), "v": v}
+    _, _, v8, _, _, sv = _gpu_prepare(inp, np.eye(d, dtype=np.float32), gpu)
+    (ov, osv) = oracle.fp8_prepare(inp["q"], inp["k"], inp["v"], np.eye(d))[2]
+    assert np.array_equal(sv, osv) and sv.reshape(-1)[0] == s
+    assert np.array_equal(v8, ov)
+
+
 def test_prepare_random_rotation(gpu):
     w = WORKLOADS["fp8_outliers_8k"].with_(B=1, H=3, N=1000)
     inp = make_inputs(w)
