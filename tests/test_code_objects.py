@@ -25,7 +25,7 @@ QUOTED = {
     "attn_mfma_bf16_seq_kernelILi64E": (154, 32768),
     "attn_mfma_bf16_seq_kernelILi128E": (256, 65536),
     "attn_fp8_kernelILi128ELb0E": (152, 32768),
-    "bwd_dkdv_kernelILi128ELi8E": (248, 132096),
+    "bwd_dkdv_kernelILi128ELi8E": (256, 132096),
     "bwd_dq_kernelILi128ELi8E": (254, 98304),
 }
 
