@@ -30,8 +30,10 @@
  *   Pointers   device pointers, 16-byte aligned, owned by the caller; the
  *              library allocates, frees and retains nothing and keeps no
  *              global state, so calls on different streams are independent.
- *              lse may be NULL (the statistic is then not written).  Inputs
- *              must not alias outputs.
+ *              The one exception is attn_bwd_static, which keeps a fixed
+ *              scratch array per GPU (see there).  lse may be NULL (the
+ *              statistic is then not written).  Inputs must not alias
+ *              outputs.
  *   Stream     a hipStream_t passed as void* (NULL = the null stream).  Every
  *              call only enqueues work and returns; the caller synchronises.
  *   Errors     a negative attn_status.  Arguments are checked on the host
