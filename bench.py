@@ -8,6 +8,11 @@ d=128, bf16.  Throughput counts 4*B*H*N^2*d FLOPs, halved for causal.
 forward's O and LSE and a seeded dO) instead, counted as 2.5 times the
 forward's FLOPs.
 
+Steps shorter than 0.2 ms (image-model rows, one-token decode) are launch
+bound: after the direct timing, the same steps are captured once into a HIP
+graph and the graph is replayed; ``config.launch`` says which was reported
+(``--launch direct`` keeps one launch per step).
+
 Prints one JSON line per workload.  ``roofline`` compares the kernel's rate
 (HIP events around the timed launches, on the launch stream) with the
 published dense matrix-core peak; ``traffic`` comes from a committed counter
@@ -152,6 +157,59 @@ def timed(step, stream, steps, warmup):
     return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
+# Steps shorter than this are launch bound: the host's per-launch cost and the
+# gaps between launches are then a visible share of the step, so the timed
+# steps are captured once into a HIP graph and replayed (each step is still
+# executed; tests/test_graph_gpu.py checks replays against eager launches).
+GRAPH_BELOW_MS = 0.2
+
+
+def timed_graph(make_step, steps, warmup):
+    """As timed(), with the K timed steps captured into one HIP graph on a
+    side stream (default priority) and replayed once."""
+    import torch
+    side = torch.cuda.Stream()
+    gstep = make_step(side)
+    for _ in range(warmup):
+        gstep()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(steps):
+            gstep()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        t_w = time.perf_counter()            # let the clocks settle: about a second of work
+        while time.perf_counter() - t_w < 1.0:
+            g.replay()
+            torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(side)
+        g.replay()
+        ev1.record(side)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
+def timed_steps(step, make_step, stream, args):
+    """Direct launches; then, for a launch-bound step that can be rebuilt on
+    another stream (make_step), the same steps replayed from a HIP graph.
+    Returns (ms_per_step, kernel_ms, launch)."""
+    ms, kms = timed(step, stream, args.steps, args.warmup)
+    if make_step is None or args.launch == "direct" or (args.launch == "auto" and ms >= GRAPH_BELOW_MS):
+        return ms, kms, "direct"
+    try:
+        gms, gkms = timed_graph(make_step, args.steps, args.warmup)
+    except RuntimeError as e:
+        print(f"bench: graph capture failed ({e}); reporting direct launches", file=sys.stderr)
+        return ms, kms, "direct"
+    return gms, gkms, "hip_graph"
+
+
 def algorithmic_bytes(w, kind: str) -> int:
     """Forward: Q, K, V read once (2 B per element in bf16, 1 B in fp8), O
     (bf16) and LSE (float32) written once; MXFP8 also reads one scale byte per
@@ -199,6 +257,7 @@ def run_workload(name, args, fp8_scales="tile"):
     stream = torch.cuda.current_stream()
     extra = {}
     extra_cfg = {}
+    make_step = None      # set where a step can be rebuilt on another stream (graph capture)
     if args.pass_ == "bwd":
         if w.dtype != "bf16":
             raise SystemExit(f"the backward pass takes bf16 workloads, not {name}")
@@ -231,13 +290,16 @@ def run_workload(name, args, fp8_scales="tile"):
         extra_cfg["input_sets"] = len(bufs)
         # arguments checked once per buffer set: a launch is then one C call,
         # so the host keeps up with the 20-30 us kernels of short sequences
-        launchers = [A.attn_fwd_launcher(qi, ki, vi, oi, li, scale=w.scale, causal=w.causal,
-                                         stream=stream) for (qi, ki, vi, oi, li) in bufs]
-        turn = [0]
+        def make_step(st):
+            launchers = [A.attn_fwd_launcher(qi, ki, vi, oi, li, scale=w.scale, causal=w.causal,
+                                             stream=st) for (qi, ki, vi, oi, li) in bufs]
+            turn = [0]
 
-        def step():
-            launchers[turn[0] % len(launchers)]()
-            turn[0] += 1
+            def one():
+                launchers[turn[0] % len(launchers)]()
+                turn[0] += 1
+            return one
+        step = make_step(stream)
     elif w.dtype == "fp8":
         mx = fp8_scales == "mx"
         kind = "mxfp8" if mx else "fp8"
@@ -264,7 +326,8 @@ def run_workload(name, args, fp8_scales="tile"):
     else:
         raise SystemExit(f"bench.py times the bf16 and fp8 workloads, not {name}")
 
-    ms_per_step, kernel_ms = timed(step, stream, args.steps, args.warmup)
+    ms_per_step, kernel_ms, launch = timed_steps(step, make_step, stream, args)
+    extra_cfg["launch"] = launch
     flops = algorithmic_flops(w, kind)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     roof, alg_bytes = roofline(w, kind, kernel_ms, peak)
@@ -339,14 +402,16 @@ def run_w4(name, args):
     n_sets = -(-INPUT_SET_BYTES // w.bytes)
     bufs = [base] + [tuple(t.clone() for t in base) for _ in range(n_sets - 1)]
     # arguments checked once per buffer set; a launch is then one C call
-    launchers = [A.w4a16_gemm_launcher(x, q, sc, z, y, group=w.G, stream=stream) for (x, q, sc, z, y) in bufs]
-    turn = [0]
+    def make_step(st):
+        launchers = [A.w4a16_gemm_launcher(x, q, sc, z, y, group=w.G, stream=st) for (x, q, sc, z, y) in bufs]
+        turn = [0]
 
-    def step():
-        launchers[turn[0] % len(launchers)]()
-        turn[0] += 1
+        def one():
+            launchers[turn[0] % len(launchers)]()
+            turn[0] += 1
+        return one
 
-    ms_per_step, kernel_ms = timed(step, stream, args.steps, args.warmup)
+    ms_per_step, kernel_ms, launch = timed_steps(make_step(stream), make_step, stream, args)
     gbs = w.bytes / (ms_per_step * 1e-3) / 1e9
     achieved = w.bytes / (kernel_ms * 1e-3) / 1e9
     line = {
@@ -357,6 +422,7 @@ def run_w4(name, args):
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "group": w.G, "seed": w.seed,
                    "bytes_per_step": w.bytes, "flops_per_step": w.flops, "input_sets": len(bufs),
+                   "launch": launch,
                    "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -382,6 +448,10 @@ def main() -> int:
                     help="fp8 workloads: one float32 scale per 128-token tile (default) or one "
                          "power-of-two scale per 32 channels of a token (MXFP8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", choices=("auto", "direct", "graph"), default="auto",
+                    help="auto: steps shorter than %.1f ms are replayed from a HIP graph "
+                         "(forward and W4A16); direct: one launch per step; graph: always replay"
+                         % GRAPH_BELOW_MS)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB per step (counter calibration)")
     args = ap.parse_args()
