@@ -78,7 +78,7 @@ def test_cpu_baseline_reports_the_oracle_sample():
     r = bench.cpu_baseline(inp, budget_s=0.0)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
-    assert r["sample"].startswith("1 of 2 heads (all 64 query rows each)")
+    assert r["sample"].startswith("1 head evaluations over the workload's 2 heads (all 64 query rows each)")
 
 
 def test_backward_is_counted_as_two_and_a_half_forwards():
@@ -95,4 +95,4 @@ def test_cpu_baseline_of_the_backward_reports_the_oracle_sample():
     w = WORKLOADS["long_causal_16k"].with_(B=1, H=2, N=64)
     r = bench.cpu_baseline_bwd(make_inputs(w), make_output_grad(w), budget_s=0.0)
     assert r["kind"] == "oracle" and r["value"] > 0
-    assert r["sample"].startswith("1 of 2 heads (dQ, dK, dV of all 64 rows each)")
+    assert r["sample"].startswith("1 head evaluations over the workload's 2 heads (dQ, dK, dV of all 64 rows")
