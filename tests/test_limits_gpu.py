@@ -11,13 +11,19 @@
   generator, one batch entry at a time; the oracle reads those bf16 values
   back for the heads it checks, so both sides see the same numbers.
 
-Gates as for the workloads: O max-abs <= 1e-2, mean-abs <= 1e-3, LSE
-max-abs <= 1e-3.
+* The backward pass on the same 4224 heads: dQ, dK, dV of three whole
+  heads against the float64 gradient oracle.
+
+Forward gates as for the workloads: O max-abs <= 1e-2, mean-abs <= 1e-3,
+LSE max-abs <= 1e-3.  Backward gates as for the long-row workloads:
+max |G - R| / max |R| <= 5e-2 and mean |G - R| / mean |R| <= 1e-2 per
+gradient tensor.
 """
 import numpy as np
 import pytest
 
 import exact_attention_127_amd as A
+import oracle
 from seeded_inputs import random_inputs
 from tests.helpers import err_stats, oracle_heads, record_parity, sample_rows, to_device
 
@@ -47,15 +53,26 @@ def test_long_sequence_sampled_rows(gpu, d):
     assert st["lse_max_abs"] <= TOL_LSE, st
 
 
+BIG = (66, 64, 4096, 128)          # B, H, N, d: more than 2^31 elements per tensor
+
+
+def _device_normal(shape, n, seed, gpu):
+    """n bf16 tensors of standard normal draws from one seeded device
+    generator, filled one batch entry at a time."""
+    import torch
+    g = torch.Generator(device=gpu)
+    g.manual_seed(seed)
+    out = [torch.empty(shape, dtype=torch.bfloat16, device=gpu) for _ in range(n)]
+    for t in out:
+        for b in range(shape[0]):
+            t[b] = torch.randn(shape[1:], generator=g, device=gpu).to(torch.bfloat16)
+    return out
+
+
 def test_many_heads_past_2_31_elements(gpu):
     import torch
-    B, H, N, d = 66, 64, 4096, 128
-    g = torch.Generator(device=gpu)
-    g.manual_seed(5100)
-    q, k, v = (torch.empty((B, H, N, d), dtype=torch.bfloat16, device=gpu) for _ in range(3))
-    for t in (q, k, v):
-        for b in range(B):
-            t[b] = torch.randn((H, N, d), generator=g, device=gpu).to(torch.bfloat16)
+    B, H, N, d = BIG
+    q, k, v = _device_normal(BIG, 3, 5100, gpu)
     assert q.numel() > 1 << 31 and (B * H - 1) * N * d > 1 << 31
     scale = d ** -0.5
     o, lse = A.attn_fwd(q, k, v, scale=scale, causal=True)
@@ -75,3 +92,28 @@ def test_many_heads_past_2_31_elements(gpu):
     assert st["max_abs"] <= TOL_MAX, st
     assert st["mean_abs"] <= TOL_MEAN, st
     assert st["lse_max_abs"] <= TOL_LSE, st
+
+
+def test_backward_many_heads_past_2_31_elements(gpu):
+    import torch
+    B, H, N, d = BIG
+    q, k, v, do = _device_normal(BIG, 4, 5200, gpu)
+    scale = d ** -0.5
+    o, lse = A.attn_fwd(q, k, v, scale=scale, causal=True)
+    dq, dk, dv = A.attn_bwd(q, k, v, o, do, lse, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(52)
+    heads = sorted({0, B * H - 1, int(rng.integers(0, B * H))})
+    for i in heads:
+        b, h = divmod(i, H)
+        x = [t[b, h].float().cpu().numpy().astype(np.float64) for t in (q, k, v, do)]
+        ref = oracle.attention_backward_head(*x, scale, True)
+        for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            gv = got[b, h].float().cpu().numpy().astype(np.float64)
+            diff = np.abs(gv - r)
+            rel_max = float(diff.max()) / max(float(np.abs(r).max()), 1e-3)
+            rel_mean = float(diff.mean()) / max(float(np.abs(r).mean()), 1e-6)
+            record_parity(f"bwd_heads_4224_N4096_d128_causal_head{i}_{name}",
+                          {"rel_max": rel_max, "rel_mean": rel_mean})
+            assert np.isfinite(gv).all(), (i, name)
+            assert rel_max <= 5e-2 and rel_mean <= 1e-2, (i, name, rel_max, rel_mean)
