@@ -117,3 +117,38 @@ def test_backward_many_heads_past_2_31_elements(gpu):
                           {"rel_max": rel_max, "rel_mean": rel_mean})
             assert np.isfinite(gv).all(), (i, name)
             assert rel_max <= 5e-2 and rel_mean <= 1e-2, (i, name, rel_max, rel_mean)
+
+
+def test_fp8_many_heads_past_2_31_elements(gpu):
+    """attn_fp8_prepare then attn_fwd_fp8 on 4224 heads of 4096 float32
+    tokens.  With a signed permutation as the rotation (exact in float32)
+    the sampled heads' e4m3 codes and tile scales equal the oracle's bit for
+    bit; the forward on them is held to the small-shape fp8 gates against
+    float64 attention on the dequantised codes."""
+    import torch
+    B, H, N, d = BIG
+    g = torch.Generator(device=gpu)
+    g.manual_seed(5300)
+    q, k, v = (torch.randn((B, H, N, d), generator=g, device=gpu) for _ in range(3))
+    rng = np.random.default_rng(53)
+    R = np.zeros((d, d), np.float32)
+    R[np.arange(d), rng.permutation(d)] = rng.choice([-1.0, 1.0], d)
+    q8, k8, v8, sq, sk, sv = A.attn_fp8_prepare(q, k, v, torch.from_numpy(R).to(gpu))
+    o, lse = A.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, scale=d ** -0.5, causal=True)
+    torch.cuda.synchronize()
+    heads = sorted({0, B * H - 1, int(rng.integers(0, B * H))})
+    pairs = [divmod(i, H) for i in heads]
+    pick = lambda t: np.stack([t[b, h].cpu().numpy() for (b, h) in pairs])[None]
+    (oq, osq), (ok, osk), (ov, osv) = oracle.fp8_prepare(pick(q), pick(k), pick(v), R)
+    for got, want in ((q8, oq), (k8, ok), (v8, ov), (sq, osq), (sk, osk), (sv, osv)):
+        assert np.array_equal(pick(got), want)
+    qd, kd, vd = (oracle.fp8_dequantize(c, s) for c, s in ((oq, osq), (ok, osk), (ov, osv)))
+    inp = {"q": qd[0][:, None], "k": kd[0][:, None], "v": vd[0][:, None], "scale": d ** -0.5, "causal": True}
+    o_ref, l_ref = oracle_heads(inp, [(i, 0) for i in range(len(pairs))])
+    od = pick(o.float())[0]
+    ld = pick(lse)[0]
+    st = err_stats(od, ld, o_ref, l_ref)
+    record_parity("fp8_heads_4224_N4096_d128_causal", st, heads=len(pairs))
+    assert np.isfinite(od).all() and np.isfinite(ld).all()
+    assert np.all(np.abs(od - o_ref) <= 6e-2 * np.maximum(1.0, np.abs(o_ref)))
+    assert st["mean_abs"] < 5e-3 and st["lse_max_abs"] < 2e-2, st
