@@ -13,6 +13,9 @@
 
 * The backward pass on the same 4224 heads: dQ, dK, dV of three whole
   heads against the float64 gradient oracle.
+* The fp8 and MXFP8 paths on 4224 heads of float32 tokens: codes and scales
+  of three whole heads bit-exact under a signed-permutation rotation, and
+  the forward on them against float64 attention on the dequantised codes.
 
 Forward gates as for the workloads: O max-abs <= 1e-2, mean-abs <= 1e-3,
 LSE max-abs <= 1e-3.  Backward gates as for the long-row workloads:
@@ -152,3 +155,45 @@ def test_fp8_many_heads_past_2_31_elements(gpu):
     assert np.isfinite(od).all() and np.isfinite(ld).all()
     assert np.all(np.abs(od - o_ref) <= 6e-2 * np.maximum(1.0, np.abs(o_ref)))
     assert st["mean_abs"] < 5e-3 and st["lse_max_abs"] < 2e-2, st
+
+
+def test_mxfp8_many_heads_past_2_31_elements(gpu):
+    """attn_mxfp8_prepare then attn_fwd_mxfp8 on the same 4224 heads: codes and
+    E8M0 scale bytes of three whole heads bit-exact under a signed-permutation
+    rotation; the forward within the element-wise bound of the MXFP8 tests
+    (bf16 rounding of P and O, float32 score sums) of float64 attention on
+    the dequantised codes."""
+    import torch
+    from tests.test_mxfp8_gpu import _acc_delta
+    B, H, N, d = BIG
+    g = torch.Generator(device=gpu)
+    g.manual_seed(5400)
+    q, k, v = (torch.randn((B, H, N, d), generator=g, device=gpu) for _ in range(3))
+    rng = np.random.default_rng(54)
+    R = np.zeros((d, d), np.float32)
+    R[np.arange(d), rng.permutation(d)] = rng.choice([-1.0, 1.0], d)
+    q8, k8, v8, sq, sk, sv = A.attn_mxfp8_prepare(q, k, v, torch.from_numpy(R).to(gpu))
+    scale = d ** -0.5
+    o, lse = A.attn_fwd_mxfp8(q8, k8, v8, sq, sk, sv, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    heads = sorted({0, B * H - 1, int(rng.integers(0, B * H))})
+    pairs = [divmod(i, H) for i in heads]
+    pick = lambda t: np.stack([t[b, h].cpu().numpy() for (b, h) in pairs])[None]
+    (oq, osq), (ok, osk), (ov, osv) = oracle.mxfp8_prepare(pick(q), pick(k), pick(v), R)
+    for got, want in ((q8, oq), (k8, ok), (v8, ov), (sq, osq), (sk, osk), (sv, osv)):
+        assert np.array_equal(pick(got), want)
+    qd, kd, vd = (oracle.dequantize_mx(c, s)[0][:, None] for c, s in ((oq, osq), (ok, osk), (ov, osv)))
+    inp = {"q": qd, "k": kd, "v": vd, "scale": scale, "causal": True}
+    hs = [(i, 0) for i in range(len(pairs))]
+    o_ref, l_ref = oracle_heads(inp, hs)
+    pv, _ = oracle_heads(inp, hs, v=np.abs(vd))
+    od = pick(o.float())[0]
+    ld = pick(lse)[0]
+    st = err_stats(od, ld, o_ref, l_ref)
+    record_parity("mxfp8_heads_4224_N4096_d128_causal", st, heads=len(pairs))
+    assert np.isfinite(od).all() and np.isfinite(ld).all()
+    for i in range(len(pairs)):
+        dl = _acc_delta(qd[i, 0], kd[i, 0], scale)
+        bound = (2.0 ** -8 + 2 * np.expm1(dl)) * pv[i] + 2.0 ** -8 * np.abs(o_ref[i]) + 1e-6
+        assert np.all(np.abs(od[i] - o_ref[i]) <= bound), i
+        assert np.abs(ld[i] - l_ref[i]).max() <= 1e-3 + dl, i
